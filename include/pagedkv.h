@@ -1,0 +1,174 @@
+/*
+ * pagedkv.h - C ABI of the paged KV-cache hot path for AMD MI355X (gfx950).
+ *
+ * Pages the operations are defined by:
+ *   [Append] "Write Triton Kv Cache Append Kernel" (skillsdirectory.com skill page)
+ *   [Paged]  "Triton KV Cache and PagedAttention" (datawhalechina llm-algo-leetcode, ch. 10)
+ *   [3bit]   "triton-3bit-kv-cache-kernel" (GitHub README)
+ *
+ * General contract (every entry point):
+ *   - Every buffer is owned by the caller.  The library never allocates or frees
+ *     memory and keeps no state between calls.  Device pointers must point to
+ *     memory of the current HIP device.
+ *   - Work is enqueued on `stream` and is asynchronous; ordering against other
+ *     streams, and against host-side updates of block tables or slot mappings,
+ *     is the caller's job (same stream => ordered).  [Append], Common failure modes.
+ *   - Arguments are validated on the host before anything is enqueued.  A
+ *     negative return value means nothing was enqueued and nothing was written:
+ *       PKV_EINVAL        malformed argument (null pointer, bad size or stride,
+ *                         misaligned pointer, Hq not a multiple of Hkv, ...)
+ *       PKV_EUNSUPPORTED  well-formed but outside the compiled set (head_dim not
+ *                         64/128, block_size not 16/32/64, group size not 1/2/4/8,
+ *                         dtype combination not provided)
+ *       PKV_EWORKSPACE    workspace missing or smaller than required
+ *       PKV_EHIP          the kernel launch itself failed (hipGetLastError)
+ *   - Strides are in ELEMENTS of the tensor's own element type (uint32 words for a
+ *     3-bit cache), never bytes.  The innermost (head_dim) stride is always 1.
+ *   - Grids depend only on the shape arguments (and max_context_len), never on
+ *     the contents of slot_mapping / context_lens, so calls can be captured in a
+ *     HIP graph at a padded maximum batch.  [Append], Performance requirements.
+ *   - Calls that share an output buffer (or a decode workspace) on different
+ *     streams without ordering race.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_EINVAL = -1,
+  PKV_EUNSUPPORTED = -2,
+  PKV_EWORKSPACE = -3,
+  PKV_EHIP = -4
+} pkv_status;
+
+typedef enum {
+  PKV_F16 = 0,         /* IEEE binary16                                             */
+  PKV_BF16 = 1,        /* bfloat16                                                  */
+  PKV_FP8_E4M3FN = 2,  /* OCP FP8 E4M3 (finite-only, max 448), one fp32 scale per row */
+  PKV_U3 = 3           /* 3-bit affine codes, 32 per 3 uint32 words, fp16 (scale, zero) per row */
+} pkv_dtype;
+
+/*
+ * kv_append - write new K and V rows into a paged block pool through slot_mapping.
+ *
+ * Defined by [Append], Required reasoning process steps 1-8 (unified prefill and
+ * decode interface; slot = block_id * block_size + slot_in_block; slot < 0 is a
+ * no-op taken before any load; K and V in one pass; scale division in fp32 before
+ * the cast), Inputs items 1-9, Kernel design rules; the packed 3-bit cache by
+ * [3bit], sections 1A/1B (bit layout) and 2, test 3 (fp16 affine scale/zero).
+ *
+ *   k_new, v_new     device, [num_tokens, num_kv_heads, head_dim] of in_dtype (F16
+ *                    or BF16); element (t, h, d) at t*stride_tok + h*stride_head + d.
+ *                    Rows must be 16-byte aligned (pointer and both strides).  May
+ *                    be views into a fused QKV buffer.
+ *   slot_mapping     device int64 [num_tokens].  slot < 0: padding, nothing of token
+ *                    t is read or written.  slot >= num_blocks*block_size: skipped
+ *                    (a caller error, handled defensively).  Two tokens with the same
+ *                    slot in one call: undefined which one wins.
+ *   k_cache, v_cache device pools [num_blocks, block_size, num_kv_heads, R] where R is
+ *                    head_dim elements (F16/BF16/FP8) or head_dim*3/32 uint32 words
+ *                    (U3); row (blk, slot, h) at blk*c_stride_block +
+ *                    c_stride_slot*slot + c_stride_head*h.  16-byte aligned rows
+ *                    (8-byte for U3 with head_dim 64).
+ *   cache_dtype      == in_dtype (bit copy), or PKV_FP8_E4M3FN, or PKV_U3.
+ *   k_meta, v_meta   FP8: fp32 [num_blocks, block_size, num_kv_heads] per-row scales
+ *                    (s = absmax/448, 1 for an all-zero row; code = RNE_e4m3fn(
+ *                    clamp(x/s, +-448))).  U3: fp16 [num_blocks, block_size,
+ *                    num_kv_heads, 2] = (s, z), per-row min/max affine parameters
+ *                    (s = fp16((max-min)/7), z = fp16(-min/s), q = clamp(rint(x/s+z),
+ *                    0, 7); degenerate rows use s = 1, z = fp16(-min)).  Contiguous.
+ *                    NULL for same-dtype caches.
+ *   head_dim         64 or 128.   block_size 16, 32 or 64.   num_tokens >= 0.
+ * Inputs must be finite for the quantised caches.  Bit-exact by contract.
+ */
+int kv_append(const void* k_new, const void* v_new, pkv_dtype in_dtype,
+              int64_t k_stride_tok, int64_t k_stride_head,
+              int64_t v_stride_tok, int64_t v_stride_head,
+              const int64_t* slot_mapping, int64_t num_tokens,
+              void* k_cache, void* v_cache, pkv_dtype cache_dtype,
+              int64_t c_stride_block, int64_t c_stride_slot, int64_t c_stride_head,
+              void* k_meta, void* v_meta,
+              int64_t num_blocks, int block_size, int num_kv_heads, int head_dim,
+              hipStream_t stream);
+
+/*
+ * paged_decode_workspace_size - bytes of workspace paged_decode needs.
+ *
+ * Split-K ("flash-decoding") partitions, named by [3bit] (title paragraph) as the
+ * form of its fused decode: the context of each request is cut into token ranges
+ * [P*i, P*(i+1)) that are processed independently and merged by log-sum-exp.
+ * Returns 0 when max_context_len <= partition size (single pass, no workspace).
+ * partition_size: 0 = automatic (the same value paged_decode picks), else a
+ * multiple of 16.  Returns (size_t)-1 for invalid arguments.
+ */
+size_t paged_decode_workspace_size(int batch, int num_q_heads, int head_dim,
+                                   int max_context_len, int partition_size);
+
+/*
+ * paged_decode - single-query attention over a paged KV cache (one decode step).
+ *
+ * Defined by [Paged], Step 1 and the reference answer (TODO 1-5): for request b and
+ * query head h, out[b,h] = sum_t softmax_t(sm_scale * q[b,h].k_t) v_t over the first
+ * context_lens[b] tokens, token t read from physical block block_tables[b, t /
+ * block_size] at slot t % block_size; GQA per [Append] (query head h reads kv head
+ * h / (num_q_heads / num_kv_heads)); with the 3-bit cache the codes are unpacked and
+ * dequantised, x = (q - z) * s, on the fly ([3bit], title paragraph, section 2 test 3).
+ *
+ *   out, q           device [batch, num_q_heads, head_dim] of q_dtype (F16 or BF16);
+ *                    element (b, h, d) at b*stride_b + h*stride_h + d; out has the
+ *                    same dtype.  16-byte aligned rows.
+ *   k_cache, v_cache pools as for kv_append; cache_dtype == q_dtype, or PKV_U3 (with
+ *                    k_meta, v_meta fp16 (s, z) as for kv_append).  PKV_FP8_E4M3FN
+ *                    decode is not provided (PKV_EUNSUPPORTED).
+ *   block_tables     device int32 [batch, bt_stride_b >= cdiv(max_context_len,
+ *                    block_size)]; entries at or beyond cdiv(context_lens[b],
+ *                    block_size) are never read.  Entries must be < num_blocks.
+ *   context_lens     device int32 [batch], 0 <= context_lens[b] <= max_context_len.
+ *                    context_lens[b] == 0 gives an all-zero output row.
+ *   sm_scale         score scale (the pages use 1/sqrt(head_dim)).
+ *   partition_size   split-K partition in tokens (0 = automatic; else a multiple of 16).
+ *   workspace        device, >= paged_decode_workspace_size(...) bytes, 256-byte
+ *                    aligned, ZERO-FILLED BEFORE ITS FIRST USE: it holds per-(b, kv
+ *                    head) arrival counters that every call leaves at zero again.
+ *                    May be NULL when the size is 0.  One workspace per stream.
+ * Accumulation is fp32; outputs are rounded to q_dtype to nearest even.
+ */
+int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
+                 int64_t q_stride_b, int64_t q_stride_h, int64_t o_stride_b, int64_t o_stride_h,
+                 const void* k_cache, const void* v_cache, pkv_dtype cache_dtype,
+                 int64_t c_stride_block, int64_t c_stride_slot, int64_t c_stride_head,
+                 const void* k_meta, const void* v_meta,
+                 const int32_t* block_tables, int64_t bt_stride_b, const int32_t* context_lens,
+                 int batch, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                 int64_t num_blocks, int max_context_len, float sm_scale, int partition_size,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pack3 / unpack3 - 3-bit packing, [3bit] sections 1A and 1B: value j of each group
+ * of 8 sits at bits 3j..3j+2 of a 24-bit little-endian octet (3 bytes); 32 values
+ * therefore fill 3 little-endian uint32 words with lane i at bit 3i.
+ *   pack3:   values  device uint8 [n_values] (only the low 3 bits are used)
+ *            -> packed device uint8 [3*n_values/8].
+ *   unpack3: packed  device uint8 [3*n_values/8] -> values device uint8 [n_values],
+ *            each in 0..7.
+ * n_values >= 0 and a multiple of 8.  No alignment requirement.  Bit-exact.
+ */
+int pack3(const uint8_t* values, uint8_t* packed, int64_t n_values, hipStream_t stream);
+int unpack3(const uint8_t* packed, uint8_t* values, int64_t n_values, hipStream_t stream);
+
+/* Human-readable text for a pkv_status value (static storage; never NULL). */
+const char* pkv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

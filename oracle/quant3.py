@@ -36,7 +36,8 @@ def quantize_u3_rows(x: np.ndarray):
     x = np.asarray(x, dtype=np.float32)
     lo = np.min(x, axis=-1)
     hi = np.max(x, axis=-1)
-    s16 = ((hi - lo) / np.float32(7.0)).astype(np.float32).astype(np.float16)
+    with np.errstate(over="ignore"):          # a range beyond fp16 becomes inf (degenerate)
+        s16 = ((hi - lo) / np.float32(7.0)).astype(np.float32).astype(np.float16)
     with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
         z16 = ((-lo) / s16.astype(np.float32)).astype(np.float32).astype(np.float16)
     bad = (s16 == 0) | ~np.isfinite(s16) | ~np.isfinite(z16)

@@ -1,0 +1,210 @@
+"""paged_kv_cache_45_amd - paged KV cache hot path for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI in include/pagedkv.h (libpagedkv.so, built in-tree
+by `paged_kv_cache_45_amd.build`).  The functions here only marshal torch tensors
+into pointers, strides and sizes and call the library; every step of the path runs
+in the HIP kernels.  There is no fallback: if the library is missing or a call fails,
+an exception is raised.
+
+Entry points (same names as the C ABI):
+    kv_append, paged_decode, paged_decode_workspace_size, pack3, unpack3,
+    pkv_status_string
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+__all__ = ["kv_append", "paged_decode", "paged_decode_workspace_size", "pack3", "unpack3",
+           "pkv_status_string", "decode_workspace", "library_path", "load_library",
+           "PKV_F16", "PKV_BF16", "PKV_FP8_E4M3FN", "PKV_U3", "PagedKVError"]
+
+PKV_F16, PKV_BF16, PKV_FP8_E4M3FN, PKV_U3 = 0, 1, 2, 3
+_STATUS = {0: "PKV_OK", -1: "PKV_EINVAL", -2: "PKV_EUNSUPPORTED", -3: "PKV_EWORKSPACE",
+           -4: "PKV_EHIP"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {_STATUS.get(status, status)} ({pkv_status_string(status)})")
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libpagedkv.so")
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libpagedkv.so.  torch is imported first so that the library binds to the HIP
+    runtime torch already loaded (same soname), and shares its streams."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    import torch  # noqa: F401  (loads torch's HIP runtime before ours)
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run paged_kv_cache_45_amd.build.build() "
+                           "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(path)
+    i64, i32, vp, f32, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
+    lib.kv_append.restype = i32
+    lib.kv_append.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, i64, vp, vp, i32, i64, i64, i64,
+                              vp, vp, i64, i32, i32, i32, vp]
+    lib.paged_decode_workspace_size.restype = sz
+    lib.paged_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.paged_decode.restype = i32
+    lib.paged_decode.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, vp, i32, i64, i64, i64, vp, vp,
+                                 vp, i64, vp, i32, i32, i32, i32, i32, i64, i32, f32, i32, vp, sz, vp]
+    lib.pack3.restype = i32
+    lib.pack3.argtypes = [vp, vp, i64, vp]
+    lib.unpack3.restype = i32
+    lib.unpack3.argtypes = [vp, vp, i64, vp]
+    lib.pkv_status_string.restype = ctypes.c_char_p
+    lib.pkv_status_string.argtypes = [i32]
+    _LIB = lib
+    return lib
+
+
+def pkv_status_string(status: int) -> str:
+    return load_library().pkv_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise PagedKVError(fn, status)
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dtype16(t) -> int:
+    import torch
+    if t.dtype == torch.float16:
+        return PKV_F16
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    raise TypeError(f"expected float16 or bfloat16, got {t.dtype}")
+
+
+def _cache_dtype(cache, ref_dtype: int, cache_dtype) -> int:
+    import torch
+    if cache_dtype is not None:
+        return {"same": ref_dtype, "fp8": PKV_FP8_E4M3FN, "u3": PKV_U3}.get(cache_dtype, cache_dtype)
+    if cache.dtype in (torch.float16, torch.bfloat16):
+        return _dtype16(cache)
+    if cache.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return PKV_FP8_E4M3FN
+    if cache.dtype in (torch.int32, torch.uint32):
+        return PKV_U3
+    raise TypeError(f"cannot infer the cache dtype from {cache.dtype}")
+
+
+def _cache_strides(k_cache, v_cache):
+    if k_cache.dim() != 4 or k_cache.stride(3) != 1:
+        raise ValueError("caches must be [num_blocks, block_size, num_kv_heads, row] with unit row stride")
+    if tuple(k_cache.stride()) != tuple(v_cache.stride()) or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape and strides")
+    return k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)
+
+
+def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_meta=None, v_meta=None,
+              cache_dtype=None, stream=None) -> None:
+    """Write new K/V [T, Hkv, D] into the paged pools through slot_mapping (int64 [T]).
+
+    Caches: [NB, BS, Hkv, D] (same dtype as the input, or uint8 fp8 codes with fp32
+    meta [NB, BS, Hkv]) or [NB, BS, Hkv, 3*D/32] int32 3-bit words with fp16 meta
+    [NB, BS, Hkv, 2]."""
+    in_dt = _dtype16(k_new)
+    if k_new.dim() != 3 or v_new.shape != k_new.shape or k_new.stride(2) != 1 or v_new.stride(2) != 1:
+        raise ValueError("k_new / v_new must be [T, Hkv, D] with unit stride on D")
+    cdt = _cache_dtype(k_cache, in_dt, cache_dtype)
+    sb, ss, sh = _cache_strides(k_cache, v_cache)
+    T, H, D = k_new.shape
+    st = load_library().kv_append(
+        _ptr(k_new), _ptr(v_new), in_dt, k_new.stride(0), k_new.stride(1), v_new.stride(0),
+        v_new.stride(1), _ptr(slot_mapping), T, _ptr(k_cache), _ptr(v_cache), cdt, sb, ss, sh,
+        _ptr(k_meta), _ptr(v_meta), k_cache.shape[0], k_cache.shape[1], H, D, _stream(stream))
+    _check("kv_append", st)
+
+
+def paged_decode_workspace_size(batch: int, num_q_heads: int, head_dim: int, max_context_len: int,
+                                partition_size: int = 0) -> int:
+    n = load_library().paged_decode_workspace_size(batch, num_q_heads, head_dim, max_context_len,
+                                                   partition_size)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid arguments to paged_decode_workspace_size")
+    return int(n)
+
+
+def decode_workspace(batch: int, num_q_heads: int, head_dim: int, max_context_len: int,
+                     partition_size: int = 0, device="cuda"):
+    """Allocate (zero-filled) the workspace paged_decode needs, or None if it needs none."""
+    import torch
+    n = paged_decode_workspace_size(batch, num_q_heads, head_dim, max_context_len, partition_size)
+    if n == 0:
+        return None
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def paged_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
+                 sm_scale: Optional[float] = None, k_meta=None, v_meta=None, partition_size: int = 0,
+                 workspace=None, out=None, cache_dtype=None, head_dim: Optional[int] = None,
+                 stream=None):
+    """Single-query paged attention: q [B, Hq, D] -> out [B, Hq, D] (q's dtype)."""
+    import torch
+    qdt = _dtype16(q)
+    if q.dim() != 3 or q.stride(2) != 1:
+        raise ValueError("q must be [B, Hq, D] with unit stride on D")
+    B, Hq, D = q.shape
+    cdt = _cache_dtype(k_cache, qdt, cache_dtype)
+    sb, ss, sh = _cache_strides(k_cache, v_cache)
+    if out is None:
+        out = torch.empty_like(q)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    if block_tables.dim() != 2 or block_tables.stride(1) != 1:
+        raise ValueError("block_tables must be [B, max_blocks] with unit stride")
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, D, max_context_len, partition_size, q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().paged_decode(
+        _ptr(out), _ptr(q), qdt, q.stride(0), q.stride(1), out.stride(0), out.stride(1),
+        _ptr(k_cache), _ptr(v_cache), cdt, sb, ss, sh, _ptr(k_meta), _ptr(v_meta),
+        _ptr(block_tables), block_tables.stride(0), _ptr(context_lens), B, Hq, k_cache.shape[2], D,
+        k_cache.shape[1], k_cache.shape[0], int(max_context_len), float(sm_scale),
+        int(partition_size), _ptr(workspace), wbytes, _stream(stream))
+    _check("paged_decode", st)
+    return out
+
+
+def pack3(values, packed=None, stream=None):
+    """uint8 values [n] (n % 8 == 0, low 3 bits used) -> uint8 packed [3n/8]."""
+    import torch
+    n = values.numel()
+    if packed is None:
+        packed = torch.empty(3 * n // 8, dtype=torch.uint8, device=values.device)
+    _check("pack3", load_library().pack3(_ptr(values), _ptr(packed), n, _stream(stream)))
+    return packed
+
+
+def unpack3(packed, n_values: Optional[int] = None, values=None, stream=None):
+    """uint8 packed [3n/8] -> uint8 values [n] in 0..7."""
+    import torch
+    n = packed.numel() * 8 // 3 if n_values is None else int(n_values)
+    if values is None:
+        values = torch.empty(n, dtype=torch.uint8, device=packed.device)
+    _check("unpack3", load_library().unpack3(_ptr(packed), _ptr(values), n, _stream(stream)))
+    return values

@@ -1,0 +1,241 @@
+// C ABI entry points: host-side validation, then dispatch to the HIP launchers.
+// Every check runs before anything is enqueued; a failing call writes nothing.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstddef>
+
+#include "../../include/pagedkv.h"
+#include "launch.h"
+
+using pkv::CacheKind;
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int log2_exact(int x) {
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return (1 << l) == x ? l : -1;
+}
+
+// head_dim / block_size: malformed (<= 0 or not a power of two) is EINVAL, a well-formed
+// value outside the compiled set is EUNSUPPORTED.
+int check_head_dim(int d) {
+  if (d <= 0) return PKV_EINVAL;
+  return (d == 64 || d == 128) ? PKV_OK : PKV_EUNSUPPORTED;
+}
+int check_block_size(int bs) {
+  if (bs <= 0 || log2_exact(bs) < 0) return PKV_EINVAL;
+  return (bs == 16 || bs == 32 || bs == 64) ? PKV_OK : PKV_EUNSUPPORTED;
+}
+bool is16(pkv_dtype t) { return t == PKV_F16 || t == PKV_BF16; }
+bool known(pkv_dtype t) { return t == PKV_F16 || t == PKV_BF16 || t == PKV_FP8_E4M3FN || t == PKV_U3; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int resolve_partition(int partition_size, int max_context_len, int batch, int num_q_heads) {
+  return partition_size == 0 ? pkv::auto_partition_size(max_context_len, batch, num_q_heads)
+                             : partition_size;
+}
+
+constexpr int kMaxPartition = 4096;   // 64 chunks of 16 tokens per wave, 4 waves
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_EINVAL: return "invalid argument";
+    case PKV_EUNSUPPORTED: return "unsupported configuration";
+    case PKV_EWORKSPACE: return "workspace missing or too small";
+    case PKV_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int pack3(const uint8_t* values, uint8_t* packed, int64_t n_values, hipStream_t stream) {
+  if (n_values < 0 || n_values % 8) return PKV_EINVAL;
+  if (n_values == 0) return PKV_OK;
+  if (!values || !packed) return PKV_EINVAL;
+  return pkv::launch_pack3(values, packed, n_values, stream) == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+int unpack3(const uint8_t* packed, uint8_t* values, int64_t n_values, hipStream_t stream) {
+  if (n_values < 0 || n_values % 8) return PKV_EINVAL;
+  if (n_values == 0) return PKV_OK;
+  if (!values || !packed) return PKV_EINVAL;
+  return pkv::launch_unpack3(packed, values, n_values, stream) == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+int kv_append(const void* k_new, const void* v_new, pkv_dtype in_dtype,
+              int64_t k_stride_tok, int64_t k_stride_head,
+              int64_t v_stride_tok, int64_t v_stride_head,
+              const int64_t* slot_mapping, int64_t num_tokens,
+              void* k_cache, void* v_cache, pkv_dtype cache_dtype,
+              int64_t c_stride_block, int64_t c_stride_slot, int64_t c_stride_head,
+              void* k_meta, void* v_meta,
+              int64_t num_blocks, int block_size, int num_kv_heads, int head_dim,
+              hipStream_t stream) {
+  if (!known(in_dtype) || !known(cache_dtype)) return PKV_EINVAL;
+  if (!is16(in_dtype)) return PKV_EUNSUPPORTED;
+  // a 16-bit cache must have the input's dtype (no implicit fp16 <-> bf16 conversion)
+  if (is16(cache_dtype) && cache_dtype != in_dtype) return PKV_EINVAL;
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0) return PKV_EINVAL;
+  int st = check_head_dim(head_dim);
+  if (st != PKV_OK) return st;
+  st = check_block_size(block_size);
+  if (st != PKV_OK) return st;
+  if (num_tokens == 0) return PKV_OK;   // nothing to read or write (source pointers may be NULL)
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PKV_EINVAL;
+  if (k_stride_tok < 0 || k_stride_head < 0 || v_stride_tok < 0 || v_stride_head < 0 ||
+      c_stride_block < 0 || c_stride_slot < 0 || c_stride_head < 0)
+    return PKV_EINVAL;
+  // 16-byte source rows (8 elements per lane)
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || k_stride_tok % 8 || k_stride_head % 8 ||
+      v_stride_tok % 8 || v_stride_head % 8)
+    return PKV_EINVAL;
+  if (!aligned(slot_mapping, 8)) return PKV_EINVAL;
+  CacheKind kind = CacheKind::Same;
+  if (cache_dtype == PKV_FP8_E4M3FN) {
+    kind = CacheKind::Fp8;
+    if (!aligned(k_cache, 8) || !aligned(v_cache, 8) || c_stride_block % 8 || c_stride_slot % 8 ||
+        c_stride_head % 8)
+      return PKV_EINVAL;
+    if (!k_meta || !v_meta || !aligned(k_meta, 4) || !aligned(v_meta, 4)) return PKV_EINVAL;
+  } else if (cache_dtype == PKV_U3) {
+    kind = CacheKind::U3;
+    if (!aligned(k_cache, 4) || !aligned(v_cache, 4)) return PKV_EINVAL;
+    if (!k_meta || !v_meta || !aligned(k_meta, 4) || !aligned(v_meta, 4)) return PKV_EINVAL;
+  } else {
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || c_stride_block % 8 ||
+        c_stride_slot % 8 || c_stride_head % 8)
+      return PKV_EINVAL;
+  }
+  pkv::AppendParams p{};
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.k_st = k_stride_tok;
+  p.k_sh = k_stride_head;
+  p.v_st = v_stride_tok;
+  p.v_sh = v_stride_head;
+  p.slots = slot_mapping;
+  p.num_tokens = num_tokens;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.c_sb = c_stride_block;
+  p.c_ss = c_stride_slot;
+  p.c_sh = c_stride_head;
+  p.k_meta = k_meta;
+  p.v_meta = v_meta;
+  p.capacity = num_blocks * block_size;
+  p.log2_bs = log2_exact(block_size);
+  p.num_kv_heads = num_kv_heads;
+  const hipError_t e = pkv::launch_append(p, kind, in_dtype == PKV_BF16, head_dim, stream);
+  return e == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+size_t paged_decode_workspace_size(int batch, int num_q_heads, int head_dim, int max_context_len,
+                                   int partition_size) {
+  if (batch < 0 || num_q_heads <= 0 || max_context_len < 0 || check_head_dim(head_dim) != PKV_OK)
+    return (size_t)-1;
+  if (partition_size < 0 || partition_size % 16 || partition_size > kMaxPartition)
+    return (size_t)-1;
+  const int ps = resolve_partition(partition_size, max_context_len, batch, num_q_heads);
+  const int64_t parts = cdiv(max_context_len, ps);
+  if (parts <= 1) return 0;
+  return (size_t)batch * num_q_heads * parts * (head_dim + 2) * sizeof(float);
+}
+
+int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
+                 int64_t q_stride_b, int64_t q_stride_h, int64_t o_stride_b, int64_t o_stride_h,
+                 const void* k_cache, const void* v_cache, pkv_dtype cache_dtype,
+                 int64_t c_stride_block, int64_t c_stride_slot, int64_t c_stride_head,
+                 const void* k_meta, const void* v_meta,
+                 const int32_t* block_tables, int64_t bt_stride_b, const int32_t* context_lens,
+                 int batch, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                 int64_t num_blocks, int max_context_len, float sm_scale, int partition_size,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!known(q_dtype) || !known(cache_dtype)) return PKV_EINVAL;
+  if (!is16(q_dtype)) return PKV_EUNSUPPORTED;
+  if (is16(cache_dtype) && cache_dtype != q_dtype) return PKV_EINVAL;
+  if (cache_dtype == PKV_FP8_E4M3FN) return PKV_EUNSUPPORTED;
+  if (batch < 0 || batch > 65535 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
+      max_context_len < 0)
+    return PKV_EINVAL;
+  if (num_q_heads % num_kv_heads) return PKV_EINVAL;
+  const int group = num_q_heads / num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8) return PKV_EUNSUPPORTED;
+  int st = check_head_dim(head_dim);
+  if (st != PKV_OK) return st;
+  st = check_block_size(block_size);
+  if (st != PKV_OK) return st;
+  if (partition_size < 0 || partition_size % 16) return PKV_EINVAL;
+  if (partition_size > kMaxPartition) return PKV_EUNSUPPORTED;
+  if (!std::isfinite(sm_scale)) return PKV_EINVAL;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_EINVAL;
+  if (q_stride_b < 0 || q_stride_h < 0 || o_stride_b < 0 || o_stride_h < 0 ||
+      c_stride_block < 0 || c_stride_slot < 0 || c_stride_head < 0)
+    return PKV_EINVAL;
+  if (!aligned(q, 16) || !aligned(out, 16) || q_stride_b % 8 || q_stride_h % 8 ||
+      o_stride_b % 8 || o_stride_h % 8)
+    return PKV_EINVAL;
+  CacheKind kind = CacheKind::Same;
+  if (cache_dtype == PKV_U3) {
+    kind = CacheKind::U3;
+    if (!aligned(k_cache, 4) || !aligned(v_cache, 4)) return PKV_EINVAL;
+    if (!k_meta || !v_meta || !aligned(k_meta, 4) || !aligned(v_meta, 4)) return PKV_EINVAL;
+  } else {
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || c_stride_block % 8 ||
+        c_stride_slot % 8 || c_stride_head % 8)
+      return PKV_EINVAL;
+  }
+  if (!aligned(block_tables, 4) || !aligned(context_lens, 4)) return PKV_EINVAL;
+  if (bt_stride_b < cdiv(max_context_len, block_size)) return PKV_EINVAL;
+  const int ps = resolve_partition(partition_size, max_context_len, batch, num_q_heads);
+  const int64_t parts = std::max<int64_t>(1, cdiv(max_context_len, ps));
+  const size_t need = paged_decode_workspace_size(batch, num_q_heads, head_dim, max_context_len,
+                                                  partition_size);
+  if (need == (size_t)-1) return PKV_EINVAL;
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+    return PKV_EWORKSPACE;
+  if (batch == 0) return PKV_OK;
+
+  pkv::DecodeParams p{};
+  p.out = out;
+  p.q = q;
+  p.q_sb = q_stride_b;
+  p.q_sh = q_stride_h;
+  p.o_sb = o_stride_b;
+  p.o_sh = o_stride_h;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.c_sb = c_stride_block;
+  p.c_ss = c_stride_slot;
+  p.c_sh = c_stride_head;
+  p.k_meta = k_meta;
+  p.v_meta = v_meta;
+  p.block_tables = block_tables;
+  p.bt_sb = bt_stride_b;
+  p.context_lens = context_lens;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.block_size = block_size;
+  p.log2_bs = log2_exact(block_size);
+  p.num_blocks = num_blocks;
+  p.max_context_len = max_context_len;
+  p.partition_size = ps;
+  p.max_parts = (int)parts;
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  if (need > 0) {
+    p.ws_acc = static_cast<float*>(workspace);
+    p.ws_ml = p.ws_acc + (int64_t)batch * num_q_heads * parts * head_dim;
+  }
+  const hipError_t e = pkv::launch_decode(p, kind, q_dtype == PKV_BF16, head_dim, group, batch, stream);
+  return e == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,176 @@
+// KV append: write new K/V rows into the paged block pool through slot_mapping.
+//
+// "Write Triton Kv Cache Append Kernel", Required reasoning process steps 1-8:
+// slot < 0 marks padding and nothing of that token is loaded; block = slot / block_size,
+// offset = slot % block_size (shift and mask, block_size a power of two); K and V are
+// written by the same thread group; quantised caches divide by the scale in fp32 and
+// only then convert.  The 3-bit cache follows "triton-3bit-kv-cache-kernel" README,
+// sections 1A/1B (bit layout) and section 2 test 3 (fp16 affine scale and zero).
+//
+// Work mapping (wave64): one (token, kv head) row per group of D/8 lanes, each lane
+// owning 8 consecutive elements (one 16-byte load of K and one of V).  A 256-thread
+// block covers 16 rows (D = 128) or 32 rows (D = 64).  The quantisers reduce over the
+// row with DPP inside the lane group, so no barrier and no LDS are involved.
+#include "launch.h"
+#include "common.cuh"
+
+namespace pkv {
+
+// OCP E4M3 (finite-only, bias 7, max 448) code of a finite fp32 value with |y| <= 448,
+// rounded to nearest even; the sign of zero is kept.
+__device__ __forceinline__ uint32_t e4m3fn_code(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  uint32_t code;
+  if (a >= 0x3C800000u) {
+    // |y| >= 2^-6, a normal e4m3 binade: keep 3 of the 23 fp32 mantissa bits, rounding the
+    // 20 dropped bits to nearest even (a carry may step into the next binade), then move
+    // the exponent bias from 127 to 7.
+    const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
+    code = r - (120u << 3);
+  } else {
+    // |y| < 2^-6: multiples of 2^-9 (subnormals, and 8 * 2^-9 = 2^-6 on round-up).
+    // The scaling by 2^9 is exact.
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  }
+  return code | sign;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void widen8(const uint4& x, float (&f)[8]) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = h_lo<BF16>(w[i]);
+    f[2 * i + 1] = h_hi<BF16>(w[i]);
+  }
+}
+
+// fp8 row: s = absmax / 448 (1 for an all-zero row), code = RNE(clamp(x / s, +-448)).
+template <int LPR, bool BF16>
+__device__ __forceinline__ void store_fp8_row(const uint4& x, uint8_t* dst, float* meta, int c) {
+  float f[8];
+  widen8<BF16>(x, f);
+  float a = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(f[e]));
+  a = group_max<LPR>(a);
+  const float s = (a == 0.f) ? 1.f : a / 448.f;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float y = f[e] / s;
+    y = fminf(fmaxf(y, -448.f), 448.f);
+    const uint32_t code = e4m3fn_code(y);
+    if (e < 4) lo |= code << (8 * e);
+    else hi |= code << (8 * (e - 4));
+  }
+  *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+  if (c == 0) *meta = s;
+}
+
+// u3 row: min/max affine parameters in fp32 rounded to fp16, codes clamp(rint(x/s + z), 0, 7),
+// 8 codes per lane = one 24-bit octet; each quad of lanes (32 values) writes 3 words.
+template <int LPR, bool BF16>
+__device__ __forceinline__ void store_u3_row(const uint4& x, uint32_t* dst_row, uint32_t* meta,
+                                             int c) {
+#pragma clang fp contract(off)
+  float f[8];
+  widen8<BF16>(x, f);
+  float lo = f[0], hi = f[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) {
+    lo = fminf(lo, f[e]);
+    hi = fmaxf(hi, f[e]);
+  }
+  lo = group_min<LPR>(lo);
+  hi = group_max<LPR>(hi);
+  _Float16 s16 = (_Float16)((hi - lo) / 7.0f);
+  float s = (float)s16;
+  _Float16 z16 = (_Float16)(-lo / s);
+  const bool bad = (s == 0.f) || !__builtin_isfinite(s) || !__builtin_isfinite((float)z16);
+  if (bad) {
+    s16 = (_Float16)1.0f;
+    s = 1.0f;
+    z16 = (_Float16)(-lo);
+  }
+  const float z = (float)z16;
+  uint32_t o = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float t = f[e] / s + z;
+    const float qf = fminf(fmaxf(__builtin_rintf(t), 0.f), 7.f);
+    o |= (uint32_t)qf << (3 * e);
+  }
+  // word j of the lane's group of 32 values: bytes 4j..4j+3 of four consecutive octets
+  const uint32_t next = dpp_u<DPP_QUAD_NEXT>(o);
+  const int j = c & 3;
+  if (j < 3) dst_row[(c >> 2) * 3 + j] = (o >> (8 * j)) | (next << (24 - 8 * j));
+  if (c == 0)
+    *meta = (uint32_t)__builtin_bit_cast(uint16_t, s16) |
+            ((uint32_t)__builtin_bit_cast(uint16_t, z16) << 16);
+}
+
+template <int D, bool BF16, CacheKind KIND>
+__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = 256 / LPR;
+  const int c = threadIdx.x % LPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int64_t t = row / p.num_kv_heads;
+  const int h = (int)(row - t * p.num_kv_heads);
+  if (t >= p.num_tokens) return;
+  const int64_t slot = p.slots[t];
+  if (slot < 0 || slot >= p.capacity) return;      // padding: no load, no store
+  const int64_t blk = slot >> p.log2_bs;
+  const int64_t off = slot & ((1 << p.log2_bs) - 1);
+  const int64_t crow = blk * p.c_sb + off * p.c_ss + (int64_t)h * p.c_sh;
+  const int64_t mrow = slot * p.num_kv_heads + h;   // meta pools are [NB, BS, Hkv] contiguous
+  const uint4 kx = *reinterpret_cast<const uint4*>(
+      static_cast<const uint16_t*>(p.k_new) + t * p.k_st + h * p.k_sh + c * 8);
+  const uint4 vx = *reinterpret_cast<const uint4*>(
+      static_cast<const uint16_t*>(p.v_new) + t * p.v_st + h * p.v_sh + c * 8);
+  if constexpr (KIND == CacheKind::Same) {
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.k_cache) + crow + c * 8) = kx;
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.v_cache) + crow + c * 8) = vx;
+  } else if constexpr (KIND == CacheKind::Fp8) {
+    store_fp8_row<LPR, BF16>(kx, static_cast<uint8_t*>(p.k_cache) + crow + c * 8,
+                             static_cast<float*>(p.k_meta) + mrow, c);
+    store_fp8_row<LPR, BF16>(vx, static_cast<uint8_t*>(p.v_cache) + crow + c * 8,
+                             static_cast<float*>(p.v_meta) + mrow, c);
+  } else {
+    store_u3_row<LPR, BF16>(kx, static_cast<uint32_t*>(p.k_cache) + crow,
+                            static_cast<uint32_t*>(p.k_meta) + mrow, c);
+    store_u3_row<LPR, BF16>(vx, static_cast<uint32_t*>(p.v_cache) + crow,
+                            static_cast<uint32_t*>(p.v_meta) + mrow, c);
+  }
+}
+
+template <int D, bool BF16, CacheKind KIND>
+static hipError_t launch_append_t(const AppendParams& p, hipStream_t s) {
+  constexpr int RPB = 256 / (D / 8);
+  const int64_t rows = p.num_tokens * p.num_kv_heads;
+  const int64_t blocks = (rows + RPB - 1) / RPB;
+  hipLaunchKernelGGL((append_kernel<D, BF16, KIND>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int D, bool BF16>
+static hipError_t dispatch_kind(const AppendParams& p, CacheKind kind, hipStream_t s) {
+  switch (kind) {
+    case CacheKind::Same: return launch_append_t<D, BF16, CacheKind::Same>(p, s);
+    case CacheKind::Fp8: return launch_append_t<D, BF16, CacheKind::Fp8>(p, s);
+    case CacheKind::U3: return launch_append_t<D, BF16, CacheKind::U3>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_append(const AppendParams& p, CacheKind kind, bool bf16, int head_dim,
+                         hipStream_t s) {
+  if (p.num_tokens == 0) return hipSuccess;
+  if (head_dim == 128) return bf16 ? dispatch_kind<128, true>(p, kind, s) : dispatch_kind<128, false>(p, kind, s);
+  return bf16 ? dispatch_kind<64, true>(p, kind, s) : dispatch_kind<64, false>(p, kind, s);
+}
+
+}  // namespace pkv

@@ -1,0 +1,104 @@
+// Device helpers shared by the paged KV-cache kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// ---------------------------------------------------------------------------------
+// 16-bit float <-> fp32.  Widening is exact; narrowing rounds to nearest even.
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+template <bool BF16>
+__device__ __forceinline__ float h_lo(uint32_t w) { return BF16 ? bf16_lo(w) : f16_lo(w); }
+template <bool BF16>
+__device__ __forceinline__ float h_hi(uint32_t w) { return BF16 ? bf16_hi(w) : f16_hi(w); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;   // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);                                 // round to nearest even
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);      // v_cvt_f16_f32, RNE
+}
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return BF16 ? (f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16))
+              : (f32_to_f16_bits(lo) | (f32_to_f16_bits(hi) << 16));
+}
+
+// Two-element dot product of packed 16-bit pairs accumulated in fp32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+template <bool BF16>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  if constexpr (BF16) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+  } else {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b),
+                                  c, false);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Cross-lane reductions inside a DPP row (16 lanes).  Every lane of the group gets
+// the result.  Group sizes 4, 8 and 16 must be aligned to the group size.
+// ---------------------------------------------------------------------------------
+enum : int {
+  DPP_QUAD_XOR1 = 0xB1,      // quad_perm [1,0,3,2]
+  DPP_QUAD_XOR2 = 0x4E,      // quad_perm [2,3,0,1]
+  DPP_QUAD_NEXT = 0xF9,      // quad_perm [1,2,3,3]: lane j reads lane j+1 of its quad
+  DPP_ROW_HALF_MIRROR = 0x141,
+  DPP_ROW_MIRROR = 0x140,
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
+}
+
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 4 || N == 8 || N == 16, "group of 4, 8 or 16 lanes");
+  x += dpp_f<DPP_QUAD_XOR1>(x);
+  x += dpp_f<DPP_QUAD_XOR2>(x);
+  if constexpr (N >= 8) x += dpp_f<DPP_ROW_HALF_MIRROR>(x);
+  if constexpr (N >= 16) x += dpp_f<DPP_ROW_MIRROR>(x);
+  return x;
+}
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  x = fmaxf(x, dpp_f<DPP_QUAD_XOR1>(x));
+  x = fmaxf(x, dpp_f<DPP_QUAD_XOR2>(x));
+  if constexpr (N >= 8) x = fmaxf(x, dpp_f<DPP_ROW_HALF_MIRROR>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dpp_f<DPP_ROW_MIRROR>(x));
+  return x;
+}
+template <int N>
+__device__ __forceinline__ float group_min(float x) {
+  x = fminf(x, dpp_f<DPP_QUAD_XOR1>(x));
+  x = fminf(x, dpp_f<DPP_QUAD_XOR2>(x));
+  if constexpr (N >= 8) x = fminf(x, dpp_f<DPP_ROW_HALF_MIRROR>(x));
+  if constexpr (N >= 16) x = fminf(x, dpp_f<DPP_ROW_MIRROR>(x));
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pkv

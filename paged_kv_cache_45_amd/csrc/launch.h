@@ -1,0 +1,63 @@
+// Internal launchers behind the C ABI (validated arguments only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+enum class CacheKind : int { Same = 0, Fp8 = 1, U3 = 2 };
+
+struct AppendParams {
+  const void* k_new;
+  const void* v_new;
+  int64_t k_st, k_sh, v_st, v_sh;     // elements
+  const int64_t* slots;
+  int64_t num_tokens;
+  void* k_cache;
+  void* v_cache;
+  int64_t c_sb, c_ss, c_sh;           // elements (bytes for fp8, words for u3)
+  void* k_meta;
+  void* v_meta;
+  int64_t capacity;                   // num_blocks * block_size
+  int log2_bs;
+  int num_kv_heads;
+};
+
+struct DecodeParams {
+  void* out;
+  const void* q;
+  int64_t q_sb, q_sh, o_sb, o_sh;     // elements
+  const void* k_cache;
+  const void* v_cache;
+  int64_t c_sb, c_ss, c_sh;           // elements (words for u3)
+  const void* k_meta;                 // u3: fp16 (s, z) per row, contiguous [NB, BS, Hkv]
+  const void* v_meta;
+  const int32_t* block_tables;
+  int64_t bt_sb;
+  const int32_t* context_lens;
+  int num_q_heads, num_kv_heads;
+  int block_size, log2_bs;
+  int64_t num_blocks;                 // block-table entries are clamped into [0, num_blocks)
+  int max_context_len;                // context lengths are clamped into [0, max_context_len]
+  int partition_size;                 // tokens, multiple of 16
+  int max_parts;                      // partitions per request in the grid
+  float scale_log2;                   // sm_scale * log2(e)
+  float* ws_acc;                      // [B, Hq, max_parts, D] (split only)
+  float* ws_ml;                       // [B, Hq, max_parts, 2]
+};
+
+hipError_t launch_pack3(const uint8_t* values, uint8_t* packed, int64_t n_values, hipStream_t s);
+hipError_t launch_unpack3(const uint8_t* packed, uint8_t* values, int64_t n_values, hipStream_t s);
+
+// bf16: true for bfloat16 inputs, false for fp16.
+hipError_t launch_append(const AppendParams& p, CacheKind kind, bool bf16, int head_dim,
+                         hipStream_t s);
+
+hipError_t launch_decode(const DecodeParams& p, CacheKind kind, bool bf16, int head_dim, int group,
+                         int batch, hipStream_t s);
+
+// Split-K partition size used when the caller passes 0.
+int auto_partition_size(int max_context_len, int batch, int num_q_heads);
+
+}  // namespace pkv

@@ -128,10 +128,12 @@ def decode_workload(name: str, *, batch: int, num_q_heads: int, num_kv_heads: in
                     block_size: int, ctx_lo: int, ctx_hi: int, dtype: torch.dtype, device,
                     seed: int, append_one: bool = True, spare_frac: float = 0.05,
                     poison: bool = True, ctx_override: Optional[List[int]] = None,
-                    min_blocks: int = 0, make_pool: bool = True) -> PagedWorkload:
+                    min_blocks: int = 0, make_pool: bool = True,
+                    data_seed: Optional[int] = None) -> PagedWorkload:
     """A decode batch: ctx ~ U{ctx_lo..ctx_hi} tokens already cached per request,
     optionally one new token per request appended at position ctx, then one query
-    token per request attending over the result."""
+    token per request attending over the result.  `seed` draws the structure (lengths,
+    block allocation); `data_seed` (default: seed) draws the tensors."""
     gen = torch.Generator().manual_seed(seed)
     if ctx_override is not None:
         ctx = list(ctx_override)
@@ -139,7 +141,7 @@ def decode_workload(name: str, *, batch: int, num_q_heads: int, num_kv_heads: in
         ctx = torch.randint(ctx_lo, ctx_hi + 1, (batch,), generator=gen).tolist()
     after = [c + 1 for c in ctx] if append_one else list(ctx)
     nb, blocks_of, bt = _allocate(after, block_size, spare_frac, gen, min_blocks)
-    dgen = _device_gen(device, seed)
+    dgen = _device_gen(device, seed if data_seed is None else data_seed)
     q = _randn((batch, num_q_heads, head_dim), dtype, device, dgen)
     k_pool = v_pool = None
     if make_pool:
@@ -196,14 +198,15 @@ def tiny(device, seed: int = BASE_SEED + 1, poison: bool = True) -> PagedWorkloa
 
 
 def llama8b_decode(device, seed: int = BASE_SEED + 2, poison: bool = True,
-                   batch: int = 64, make_pool: bool = True) -> PagedWorkload:
+                   batch: int = 64, make_pool: bool = True,
+                   data_seed: Optional[int] = None) -> PagedWorkload:
     """Llama-8B-shaped decode step: B=64, 32 q heads / 8 kv heads, D=128, BS=16,
     bf16, ctx ~ U{512..4096}, one token appended per request, shuffled pool with
     5% spare (poisoned) blocks."""
     return decode_workload("llama8b-decode", batch=batch, num_q_heads=32, num_kv_heads=8,
                            head_dim=128, block_size=16, ctx_lo=512, ctx_hi=4096,
                            dtype=torch.bfloat16, device=device, seed=seed, poison=poison,
-                           make_pool=make_pool)
+                           make_pool=make_pool, data_seed=data_seed)
 
 
 def long_context(device, seed: int = BASE_SEED + 4, poison: bool = False,
