@@ -200,6 +200,7 @@ int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
   const size_t need = paged_decode_workspace_size(batch, num_q_heads, head_dim, max_context_len,
                                                   partition_size);
   if (need == (size_t)-1) return PKV_EINVAL;
+  if (parts * num_kv_heads * batch > 0x7fffffffLL) return PKV_EUNSUPPORTED;
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
     return PKV_EWORKSPACE;
   if (batch == 0) return PKV_OK;
@@ -223,6 +224,7 @@ int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
   p.context_lens = context_lens;
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = num_kv_heads;
+  p.batch = batch;
   p.block_size = block_size;
   p.log2_bs = log2_exact(block_size);
   p.num_blocks = num_blocks;

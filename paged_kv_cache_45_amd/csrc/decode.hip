@@ -11,7 +11,8 @@
 // dequantised, x = (q - z) * s, in registers.
 //
 // MI355X mapping:
-//  * grid (partition, kv head, request); one 4-wave workgroup owns the token range
+//  * one 4-wave workgroup per (kv head, request, partition), kv head fastest in the
+//    flattened grid (balances the XCDs); the workgroup owns the token range
 //    [partition * P, (partition + 1) * P) of one (request, kv head) and all G query heads
 //    of that kv head, so every K/V byte is read from HBM once.
 //  * The range is cut into 16-token chunks (a block holds 1, 2 or 4 of them); wave w takes
@@ -61,9 +62,14 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams p) {
   const int w = threadIdx.x >> 6;
   const int r = lane / LPR;
   const int c = lane % LPR;
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
+  // Flattened grid, kv head fastest: consecutive workgroup ids go round-robin to the 8 XCDs,
+  // so with Hkv = 8 each XCD owns one kv head of every (request, partition) and all XCDs
+  // get the same work; partitions vary slowest, so the mostly-empty high partitions of
+  // short requests come last.
+  const int64_t wg = blockIdx.x;
+  const int kvh = (int)(wg % p.num_kv_heads);
+  const int b = (int)((wg / p.num_kv_heads) % p.batch);
+  const int part = (int)(wg / ((int64_t)p.num_kv_heads * p.batch));
   const int h0 = kvh * G;
   // out-of-contract lengths are clamped so that no access leaves the grid's buffers
   const int ctx = min(max(p.context_lens[b], 0), p.max_context_len);
@@ -346,8 +352,9 @@ __global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
 
 template <int D, int G, bool BF16, CacheKind KIND>
 static hipError_t launch_t(const DecodeParams& p, int batch, hipStream_t s) {
-  const dim3 grid((unsigned)p.max_parts, (unsigned)p.num_kv_heads, (unsigned)batch);
-  hipLaunchKernelGGL((decode_kernel<D, G, BF16, KIND>), grid, dim3(kWaves * 64), 0, s, p);
+  const int64_t wgs = (int64_t)p.max_parts * p.num_kv_heads * batch;
+  hipLaunchKernelGGL((decode_kernel<D, G, BF16, KIND>), dim3((unsigned)wgs), dim3(kWaves * 64), 0, s,
+                     p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.max_parts <= 1) return e;
   hipLaunchKernelGGL((merge_kernel<D, BF16>), dim3((unsigned)p.num_q_heads, (unsigned)batch),

@@ -37,6 +37,7 @@ struct DecodeParams {
   int64_t bt_sb;
   const int32_t* context_lens;
   int num_q_heads, num_kv_heads;
+  int batch;
   int block_size, log2_bs;
   int64_t num_blocks;                 // block-table entries are clamped into [0, num_blocks)
   int max_context_len;                // context lengths are clamped into [0, max_context_len]
