@@ -102,7 +102,8 @@ def main():
     maxctx = max(w.max_context_len for w in layers)
     dev = [dict(bt=w.block_tables.cuda(), ctx=w.ctx_after.cuda(), slots=w.slot_mapping.cuda(),
                 out=torch.empty_like(w.q),
-                ws=P.decode_workspace(B, Hq, D, maxctx, args.partition_size)) for w in layers]
+                ws=P.decode_workspace(B, Hq, wl0.num_kv_heads, D, maxctx, args.partition_size))
+           for w in layers]
     stream = torch.cuda.current_stream()
 
     def step(i, ev=None):

@@ -102,14 +102,18 @@ int kv_append(const void* k_new, const void* v_new, pkv_dtype in_dtype,
 /*
  * paged_decode_workspace_size - bytes of workspace paged_decode needs.
  *
- * Split-K ("flash-decoding") partitions, named by [3bit] (title paragraph) as the
- * form of its fused decode: the context of each request is cut into token ranges
- * [P*i, P*(i+1)) that are processed independently and merged by log-sum-exp.
- * Returns 0 when max_context_len <= partition size (single pass, no workspace).
- * partition_size: 0 = automatic (the same value paged_decode picks), else a
- * multiple of 16.  Returns (size_t)-1 for invalid arguments.
+ * Split-K ("flash-decoding", named by [3bit] in its title paragraph as the form of its fused
+ * decode): the context of each (request, kv head) may be cut into token ranges that are
+ * reduced independently and merged by log-sum-exp.  The library balances the work by
+ * giving each resident wave of the current device an equal share of all
+ * (request, kv head, granule) units, where a granule is `partition_size` tokens; a context
+ * is only ever cut at a multiple of the granule.  The workspace holds the partial states
+ * of the ranges that get cut, so its size depends on the current device's compute-unit
+ * count: query it on the device that will run the call.
+ * partition_size: 0 = automatic (16 tokens, the finest balance), else a multiple of 16.
+ * Returns 0 for batch 0 and (size_t)-1 for invalid arguments (batch above 8192 included).
  */
-size_t paged_decode_workspace_size(int batch, int num_q_heads, int head_dim,
+size_t paged_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                                    int max_context_len, int partition_size);
 
 /*
@@ -134,11 +138,12 @@ size_t paged_decode_workspace_size(int batch, int num_q_heads, int head_dim,
  *   context_lens     device int32 [batch], 0 <= context_lens[b] <= max_context_len.
  *                    context_lens[b] == 0 gives an all-zero output row.
  *   sm_scale         score scale (the pages use 1/sqrt(head_dim)).
- *   partition_size   split-K partition in tokens (0 = automatic; else a multiple of 16).
- *   workspace        device, >= paged_decode_workspace_size(...) bytes, 256-byte
- *                    aligned, ZERO-FILLED BEFORE ITS FIRST USE: it holds per-(b, kv
- *                    head) arrival counters that every call leaves at zero again.
- *                    May be NULL when the size is 0.  One workspace per stream.
+ *   partition_size   split granule in tokens (0 = automatic; else a multiple of 16); see
+ *                    paged_decode_workspace_size.
+ *   workspace        device, >= paged_decode_workspace_size(...) bytes, 256-byte aligned,
+ *                    no initialisation needed (every call overwrites what it reads).
+ *                    One workspace per stream: calls sharing it must be ordered.
+ *   batch            0 .. 8192.
  * Accumulation is fp32; outputs are rounded to q_dtype to nearest even.
  */
 int paged_decode(void* out, const void* q, pkv_dtype q_dtype,

@@ -56,7 +56,7 @@ def load_library() -> ctypes.CDLL:
     lib.kv_append.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, i64, vp, vp, i32, i64, i64, i64,
                               vp, vp, i64, i32, i32, i32, vp]
     lib.paged_decode_workspace_size.restype = sz
-    lib.paged_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.paged_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.paged_decode.restype = i32
     lib.paged_decode.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, vp, i32, i64, i64, i64, vp, vp,
                                  vp, i64, vp, i32, i32, i32, i32, i32, i64, i32, f32, i32, vp, sz, vp]
@@ -140,23 +140,24 @@ def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_meta=None, v_meta=
     _check("kv_append", st)
 
 
-def paged_decode_workspace_size(batch: int, num_q_heads: int, head_dim: int, max_context_len: int,
-                                partition_size: int = 0) -> int:
-    n = load_library().paged_decode_workspace_size(batch, num_q_heads, head_dim, max_context_len,
-                                                   partition_size)
+def paged_decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                                max_context_len: int, partition_size: int = 0) -> int:
+    n = load_library().paged_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim,
+                                                   max_context_len, partition_size)
     if n == ctypes.c_size_t(-1).value:
         raise ValueError("invalid arguments to paged_decode_workspace_size")
     return int(n)
 
 
-def decode_workspace(batch: int, num_q_heads: int, head_dim: int, max_context_len: int,
-                     partition_size: int = 0, device="cuda"):
-    """Allocate (zero-filled) the workspace paged_decode needs, or None if it needs none."""
+def decode_workspace(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                     max_context_len: int, partition_size: int = 0, device="cuda"):
+    """Allocate the workspace paged_decode needs on `device` (None if it needs none)."""
     import torch
-    n = paged_decode_workspace_size(batch, num_q_heads, head_dim, max_context_len, partition_size)
+    n = paged_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                                    partition_size)
     if n == 0:
         return None
-    return torch.zeros(n, dtype=torch.uint8, device=device)
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def paged_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
@@ -178,7 +179,8 @@ def paged_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_le
     if block_tables.dim() != 2 or block_tables.stride(1) != 1:
         raise ValueError("block_tables must be [B, max_blocks] with unit stride")
     if workspace is None:
-        workspace = decode_workspace(B, Hq, D, max_context_len, partition_size, q.device)
+        workspace = decode_workspace(B, Hq, k_cache.shape[2], D, max_context_len, partition_size,
+                                     q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load_library().paged_decode(
         _ptr(out), _ptr(q), qdt, q.stride(0), q.stride(1), out.stride(0), out.stride(1),

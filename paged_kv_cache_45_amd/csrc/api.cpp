@@ -40,7 +40,28 @@ int resolve_partition(int partition_size, int max_context_len, int batch, int nu
                              : partition_size;
 }
 
-constexpr int kMaxPartition = 4096;   // 64 chunks of 16 tokens per wave, 4 waves
+constexpr int kMaxPartition = 1 << 20;
+constexpr int kMaxBatch = 8192;       // the decode kernel keeps batch + 1 prefix sums in LDS
+
+struct DecodeLayout {
+  pkv::DecodePlan plan;
+  size_t acc_off, ml_off, prefix_off, bytes;
+};
+
+// Workspace layout of paged_decode: partial accumulators, partial (m, l), prefix sums.
+DecodeLayout decode_layout(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                           int max_context_len, int ps, int bf16, int kind) {
+  DecodeLayout L{};
+  const int64_t group = num_q_heads / num_kv_heads;
+  L.plan = pkv::plan_decode(batch, num_q_heads, num_kv_heads, head_dim, max_context_len, ps, bf16, kind);
+  const size_t slots = (size_t)L.plan.num_wgs * 2 * L.plan.heads_per_group * group;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  L.acc_off = 0;
+  L.ml_off = up(slots * head_dim * sizeof(float));
+  L.prefix_off = L.ml_off + up(slots * 2 * sizeof(float));
+  L.bytes = L.prefix_off + up((size_t)(batch + 1) * sizeof(int));
+  return L;
+}
 
 }  // namespace
 
@@ -138,16 +159,16 @@ int kv_append(const void* k_new, const void* v_new, pkv_dtype in_dtype,
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
-size_t paged_decode_workspace_size(int batch, int num_q_heads, int head_dim, int max_context_len,
-                                   int partition_size) {
-  if (batch < 0 || num_q_heads <= 0 || max_context_len < 0 || check_head_dim(head_dim) != PKV_OK)
+size_t paged_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
+                                   int max_context_len, int partition_size) {
+  if (batch < 0 || batch > kMaxBatch || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads || max_context_len < 0 || check_head_dim(head_dim) != PKV_OK)
     return (size_t)-1;
   if (partition_size < 0 || partition_size % 16 || partition_size > kMaxPartition)
     return (size_t)-1;
   const int ps = resolve_partition(partition_size, max_context_len, batch, num_q_heads);
-  const int64_t parts = cdiv(max_context_len, ps);
-  if (parts <= 1) return 0;
-  return (size_t)batch * num_q_heads * parts * (head_dim + 2) * sizeof(float);
+  if (batch == 0) return 0;
+  return decode_layout(batch, num_q_heads, num_kv_heads, head_dim, max_context_len, ps, -1, -1).bytes;
 }
 
 int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
@@ -163,9 +184,9 @@ int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
   if (!is16(q_dtype)) return PKV_EUNSUPPORTED;
   if (is16(cache_dtype) && cache_dtype != q_dtype) return PKV_EINVAL;
   if (cache_dtype == PKV_FP8_E4M3FN) return PKV_EUNSUPPORTED;
-  if (batch < 0 || batch > 65535 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
-      max_context_len < 0)
+  if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_context_len < 0)
     return PKV_EINVAL;
+  if (batch > kMaxBatch) return PKV_EUNSUPPORTED;
   if (num_q_heads % num_kv_heads) return PKV_EINVAL;
   const int group = num_q_heads / num_kv_heads;
   if (group != 1 && group != 2 && group != 4 && group != 8) return PKV_EUNSUPPORTED;
@@ -194,16 +215,17 @@ int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
       return PKV_EINVAL;
   }
   if (!aligned(block_tables, 4) || !aligned(context_lens, 4)) return PKV_EINVAL;
+  // per-lane row offsets inside a 16-slot chunk are 32-bit byte offsets
+  if ((c_stride_slot * 16 + c_stride_head * (int64_t)num_kv_heads) * 4 >= 0x7fffffffLL)
+    return PKV_EUNSUPPORTED;
   if (bt_stride_b < cdiv(max_context_len, block_size)) return PKV_EINVAL;
   const int ps = resolve_partition(partition_size, max_context_len, batch, num_q_heads);
-  const int64_t parts = std::max<int64_t>(1, cdiv(max_context_len, ps));
-  const size_t need = paged_decode_workspace_size(batch, num_q_heads, head_dim, max_context_len,
-                                                  partition_size);
-  if (need == (size_t)-1) return PKV_EINVAL;
-  if (parts * num_kv_heads * batch > 0x7fffffffLL) return PKV_EUNSUPPORTED;
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
-    return PKV_EWORKSPACE;
+  // granule counts and indices stay in 32 bits
+  if ((int64_t)batch * num_kv_heads * cdiv(max_context_len, ps) > 0x7fffffffLL) return PKV_EUNSUPPORTED;
   if (batch == 0) return PKV_OK;
+  const DecodeLayout L = decode_layout(batch, num_q_heads, num_kv_heads, head_dim, max_context_len, ps,
+                                       q_dtype == PKV_BF16 ? 1 : 0, kind == CacheKind::U3 ? 1 : 0);
+  if (!workspace || workspace_bytes < L.bytes || !aligned(workspace, 256)) return PKV_EWORKSPACE;
 
   pkv::DecodeParams p{};
   p.out = out;
@@ -230,13 +252,16 @@ int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
   p.num_blocks = num_blocks;
   p.max_context_len = max_context_len;
   p.partition_size = ps;
-  p.max_parts = (int)parts;
+  p.num_wgs = L.plan.num_wgs;
+  p.heads_per_group = L.plan.heads_per_group;
+  p.num_head_groups = L.plan.num_head_groups;
+  p.token_streams = L.plan.token_streams;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
-  if (need > 0) {
-    p.ws_acc = static_cast<float*>(workspace);
-    p.ws_ml = p.ws_acc + (int64_t)batch * num_q_heads * parts * head_dim;
-  }
-  const hipError_t e = pkv::launch_decode(p, kind, q_dtype == PKV_BF16, head_dim, group, batch, stream);
+  char* ws = static_cast<char*>(workspace);
+  p.ws_acc = reinterpret_cast<float*>(ws + L.acc_off);
+  p.ws_ml = reinterpret_cast<float*>(ws + L.ml_off);
+  p.ws_prefix = reinterpret_cast<int*>(ws + L.prefix_off);
+  const hipError_t e = pkv::launch_decode(p, L.plan, kind, q_dtype == PKV_BF16, head_dim, group, stream);
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 

@@ -1,4 +1,4 @@
-// Paged decode attention (one query token per request) with split-K partitions.
+// Paged decode attention (one query token per request), balanced split-K.
 //
 // What is computed ("Triton KV Cache and PagedAttention", Step 1 and the reference
 // answer, TODO 1-5): for request b and query head h, out = sum_t softmax_t(sm_scale *
@@ -8,393 +8,676 @@
 // accumulator).  GQA ("Write Triton Kv Cache Append Kernel", Kernel design rules): the G =
 // Hq / Hkv query heads h = kvh*G .. kvh*G+G-1 share kv head kvh.  The 3-bit cache
 // ("triton-3bit-kv-cache-kernel" README, title paragraph and section 2) is unpacked and
-// dequantised, x = (q - z) * s, in registers.
+// dequantised, x = (q - z) * s, in registers.  Split-K: the context of a (request, kv head)
+// may be cut at multiples of the partition size into ranges that are reduced separately
+// and merged by log-sum-exp (the flash-decoding form the 3-bit README names).
 //
 // MI355X mapping:
-//  * one 4-wave workgroup per (kv head, request, partition), kv head fastest in the
-//    flattened grid (balances the XCDs); the workgroup owns the token range
-//    [partition * P, (partition + 1) * P) of one (request, kv head) and all G query heads
-//    of that kv head, so every K/V byte is read from HBM once.
-//  * The range is cut into 16-token chunks (a block holds 1, 2 or 4 of them); wave w takes
-//    chunks w, w+4, ...  The physical block of each of a wave's chunks is fetched once up
-//    front into one VGPR (lane k = k-th chunk) and read back with v_readlane.
-//  * Lane layout: D/8 lanes per token row, each lane owning 8 consecutive elements
-//    (16 bytes of K and of V, one global_load_dwordx4 each); a wave instruction covers
-//    4 (D = 128) or 8 (D = 64) token rows.
-//  * QK: v_dot2_f32_{bf16,f16} on the packed pairs, then a DPP reduction inside the lane
-//    group; every lane of a row ends with the row's scores for all G heads.
-//  * Each token row keeps its own online-softmax state (m, l in log2 units, and the
-//    lane's 8 accumulator columns per head); rows are merged with shuffles at the end,
-//    the 4 waves through LDS.
-//  * Partitions of one request are merged by log-sum-exp in a second small kernel; a
-//    request that fits in one partition writes its output directly.
+//  * Memory: one slot of a block stores all kv heads of a token contiguously
+//    ([block, slot, head, d]).  A wave instruction reads HPI heads x D elements of one
+//    token (1 KB for 4 heads of 128 bf16), and the waves of a workgroup cover the other
+//    heads of the same tokens at the same time, so whole slot rows are streamed and each
+//    opened DRAM page is used in full.  Lane layout: D/8 lanes per (head, token) row, each
+//    lane owning 8 consecutive elements (one 16-byte load of K and one of V).
+//  * Work (stream-K): requests are cut into granules of `partition_size` tokens; the
+//    (request, head group, granule) units are laid end to end and the grid holds as many
+//    workgroups as the chip keeps resident, each taking an equal contiguous range of
+//    units.  All workgroups stream for the same time, with no tail.  A (request, head
+//    group) segment covered by one workgroup is finished in registers; where a range starts
+//    or ends inside a segment the partial state (m, l, acc) goes to the workspace and a
+//    small second kernel merges it by log-sum-exp.
+//  * QK: v_dot2_f32_{bf16,f16} on packed pairs and a DPP reduction inside the lane row;
+//    each row keeps its own online-softmax state (m, l in log2 units, the lane's 8
+//    accumulator columns per query head).
+//  * Physical block ids of up to 64 chunks are fetched with one vector load (lane k <->
+//    k-th chunk) and read back with v_readlane.
+#include <algorithm>
+#include <type_traits>
+
 #include "launch.h"
 #include "common.cuh"
 
 namespace pkv {
 
-constexpr int kWaves = 4;           // waves per workgroup
-constexpr int kChunk = 16;          // tokens per chunk
+constexpr int kMaxWaves = 8;        // waves per workgroup at most (token streams x head group)
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 
-// Combine two online-softmax states (m in log2 units).  Returns the factors that scale
-// each side's (l, acc) to the common maximum.
-__device__ __forceinline__ void lse_factors(float ma, float mb, float& m, float& fa, float& fb) {
-  m = fmaxf(ma, mb);
-  const float mu = (m == neg_inf()) ? 0.f : m;
-  fa = fast_exp2(ma - mu);
-  fb = fast_exp2(mb - mu);
+__device__ __forceinline__ int clamp_ctx(const DecodeParams& p, int b) {
+  return min(max(p.context_lens[b], 0), p.max_context_len);
 }
 
-template <int D, int G, bool BF16, CacheKind KIND>
-__global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeParams p) {
-  constexpr int LPR = D / 8;           // lanes per token row
-  constexpr int RPI = 64 / LPR;        // token rows per wave instruction
-  constexpr int NI = kChunk / RPI;     // wave instructions per chunk
-  static_assert(KIND == CacheKind::Same || KIND == CacheKind::U3, "decode cache kind");
+// Lane geometry for head_dim D with HPI heads per wave instruction.
+template <int D, int HPI>
+struct Geo {
+  static constexpr int LPR = D / 8;                 // lanes per (head, token) row
+  static constexpr int RPI = 64 / LPR;              // rows per wave instruction
+  static constexpr int TPI = RPI / HPI;             // tokens per wave instruction
+  static constexpr int NI = (16 / TPI) < 4 ? (16 / TPI) : 4;   // instructions per chunk
+  static constexpr int CT = NI * TPI;               // tokens per chunk (divides 16)
+  static_assert(RPI % HPI == 0 && 16 % CT == 0, "lane geometry");
+};
 
-  __shared__ float sm_acc[kWaves][G][D];
-  __shared__ float sm_m[kWaves][G];
-  __shared__ float sm_l[kWaves][G];
+template <int NI, CacheKind KIND> struct Regs;
+template <int NI> struct Regs<NI, CacheKind::Same> { uint4 k[NI], v[NI]; };
+template <int NI> struct Regs<NI, CacheKind::U3> {
+  uint32_t klo[NI], khi[NI], vlo[NI], vhi[NI], km[NI], vm[NI];
+};
 
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int r = lane / LPR;
-  const int c = lane % LPR;
-  // Flattened grid, kv head fastest: consecutive workgroup ids go round-robin to the 8 XCDs,
-  // so with Hkv = 8 each XCD owns one kv head of every (request, partition) and all XCDs
-  // get the same work; partitions vary slowest, so the mostly-empty high partitions of
-  // short requests come last.
-  const int64_t wg = blockIdx.x;
-  const int kvh = (int)(wg % p.num_kv_heads);
-  const int b = (int)((wg / p.num_kv_heads) % p.batch);
-  const int part = (int)(wg / ((int64_t)p.num_kv_heads * p.batch));
-  const int h0 = kvh * G;
-  // out-of-contract lengths are clamped so that no access leaves the grid's buffers
-  const int ctx = min(max(p.context_lens[b], 0), p.max_context_len);
-  const int nparts = (ctx + p.partition_size - 1) / p.partition_size;
-
-  if (part >= nparts) {
-    if (part == 0) {                   // empty context: the output row is zero
-      for (int i = threadIdx.x; i < G * D; i += kWaves * 64)
-        static_cast<uint16_t*>(p.out)[b * p.o_sb + (int64_t)(h0 + i / D) * p.o_sh + i % D] = 0;
-    }
-    return;
-  }
-  const int t_begin = part * p.partition_size;
-  const int t_end = min(ctx, t_begin + p.partition_size);
-  const int nchunks = (t_end - t_begin + kChunk - 1) / kChunk;
-
-  // The G query rows of this kv head, this lane's 8 elements.
-  uint32_t qv[G][4];
-  float qsum[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) +
-                                                    b * p.q_sb + (int64_t)(h0 + g) * p.q_sh + c * 8);
-    qv[g][0] = v.x; qv[g][1] = v.y; qv[g][2] = v.z; qv[g][3] = v.w;
-    qsum[g] = 0.f;
-    if constexpr (KIND == CacheKind::U3) {
-      float s = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s += h_lo<BF16>(qv[g][e]) + h_hi<BF16>(qv[g][e]);
-      qsum[g] = group_sum<LPR>(s);
-    }
-  }
-
-  // Physical block of each of this wave's chunks (lane k <-> k-th chunk of the wave).
-  int bt_lane = 0;
-  {
-    const int ck = w + lane * kWaves;
-    if (ck < nchunks) {
-      const int e = p.block_tables[b * p.bt_sb + ((t_begin + ck * kChunk) >> p.log2_bs)];
-      bt_lane = (int)min<int64_t>(max(e, 0), p.num_blocks - 1);   // out-of-range ids clamped
-    }
-  }
-
+template <int G>
+struct State {
+  uint32_t qv[G][4];                 // this lane's 8 query elements of each query head
+  float qsum[G];                     // u3: sum of the query row (dequant hoisting)
   float m[G], l[G], zc[G], acc[G][8];
+};
+
+// Per-lane byte offsets of the rows a lane reads in a chunk (instruction i reads the row
+// TPI*i slots after the lane's first row); the chunk's block and first slot are
+// wave-uniform and kept in scalar registers.
+template <int D, int HPI, CacheKind KIND>
+struct LaneOffsets {
+  static constexpr int NI = Geo<D, HPI>::NI;
+  uint32_t row[NI];                  // bytes from the chunk's uniform row base
+  uint32_t meta[NI];                 // u3: bytes from the chunk's uniform meta base
+};
+
+template <int D, int HPI, CacheKind KIND>
+__device__ __forceinline__ LaneOffsets<D, HPI, KIND> lane_offsets(const DecodeParams& p, int tr, int hh,
+                                                                   int c) {
+  using Gm = Geo<D, HPI>;
+  LaneOffsets<D, HPI, KIND> o;
+  constexpr int esz = KIND == CacheKind::U3 ? 4 : 2;
+  const int col = KIND == CacheKind::U3 ? ((3 * c) >> 2) : c * 8;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = neg_inf();
-    l[g] = 0.f;
-    zc[g] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[g][e] = 0.f;
+  for (int i = 0; i < Gm::NI; ++i) {
+    const int64_t slot = tr + i * Gm::TPI;
+    o.row[i] = (uint32_t)((slot * p.c_ss + (int64_t)hh * p.c_sh + col) * esz);
+    o.meta[i] = (uint32_t)((slot * p.num_kv_heads + hh) * 4);
   }
+  return o;
+}
 
-  const int64_t head_off = (int64_t)kvh * p.c_sh;
-  for (int k = 0, ck = w; ck < nchunks; ++k, ck += kWaves) {
-    const int tok0 = t_begin + ck * kChunk;
-    const int phys = __builtin_amdgcn_readlane(bt_lane, k);
-    const int slot0 = (tok0 & (p.block_size - 1)) + r;       // this row's slot at i = 0
-    const int64_t row0 = (int64_t)phys * p.c_sb + (int64_t)slot0 * p.c_ss + head_off;
-
-    bool valid[NI];
+// Issue the loads of one chunk: `kb`/`vb` point at the row of (block, first slot, first head
+// of the group) and `kmb`/`vmb` at its meta entry (u3), all wave-uniform.
+template <int D, int HPI, CacheKind KIND>
+__device__ __forceinline__ void load_chunk(const char* kb, const char* vb, const char* kmb,
+                                           const char* vmb, const LaneOffsets<D, HPI, KIND>& o, int c,
+                                           Regs<Geo<D, HPI>::NI, KIND>& R) {
+  using Gm = Geo<D, HPI>;
+  if constexpr (KIND == CacheKind::Same) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) valid[i] = tok0 + i * RPI + r < t_end;
-
-    float sc[NI][G];
-    float vf[NI][8];                 // V values (Same) or codes (U3)
-    float vs[NI], vz[NI];            // U3: V scale / zero of the row
-    if constexpr (KIND == CacheKind::Same) {
-      uint4 kr[NI], vr[NI];
-      const uint16_t* kb = static_cast<const uint16_t*>(p.k_cache) + row0 + c * 8;
-      const uint16_t* vb = static_cast<const uint16_t*>(p.v_cache) + row0 + c * 8;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        kr[i] = *reinterpret_cast<const uint4*>(kb + (int64_t)i * RPI * p.c_ss);
-        vr[i] = *reinterpret_cast<const uint4*>(vb + (int64_t)i * RPI * p.c_ss);
-      }
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const uint32_t kw[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float d = 0.f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) d = dot2<BF16>(qv[g][e], kw[e], d);
-          d = group_sum<LPR>(d);
-          sc[i][g] = valid[i] ? d * p.scale_log2 : neg_inf();
-        }
-        const uint32_t vw[4] = {valid[i] ? vr[i].x : 0u, valid[i] ? vr[i].y : 0u,
-                                valid[i] ? vr[i].z : 0u, valid[i] ? vr[i].w : 0u};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vf[i][2 * e] = h_lo<BF16>(vw[e]);
-          vf[i][2 * e + 1] = h_hi<BF16>(vw[e]);
-        }
-      }
-    } else {
-      // 3-bit rows: D*3/32 words; lane c owns octet c = stream bits [24c, 24c + 24), which
-      // start in word 3c/4 at bit 24c mod 32 and spill into the next word for c mod 4 in {1, 2}.
-      constexpr int WPR = D * 3 / 32;
-      const int wj = (3 * c) >> 2;
-      const int sh = (24 * c) & 31;
-      const bool two = ((c & 3) == 1) || ((c & 3) == 2);
-      const uint32_t* kb = static_cast<const uint32_t*>(p.k_cache) + row0 + wj;
-      const uint32_t* vb = static_cast<const uint32_t*>(p.v_cache) + row0 + wj;
-      const int64_t mbase = ((int64_t)phys * p.block_size + slot0) * p.num_kv_heads + kvh;
-      const uint32_t* km = static_cast<const uint32_t*>(p.k_meta) + mbase;
-      const uint32_t* vm = static_cast<const uint32_t*>(p.v_meta) + mbase;
-      uint32_t klo[NI], khi[NI], vlo[NI], vhi[NI], kmeta[NI], vmeta[NI];
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int64_t ro = (int64_t)i * RPI * p.c_ss;
-        klo[i] = kb[ro];
-        khi[i] = two ? kb[ro + 1] : 0u;
-        vlo[i] = vb[ro];
-        vhi[i] = two ? vb[ro + 1] : 0u;
-        const int64_t mo = (int64_t)i * RPI * p.num_kv_heads;
-        kmeta[i] = km[mo];
-        vmeta[i] = vm[mo];
-      }
-      (void)WPR;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const uint32_t ko = __builtin_amdgcn_alignbit(khi[i], klo[i], sh) & 0xffffffu;
-        const float ks = f16_lo(kmeta[i]), kz = f16_hi(kmeta[i]);
-        // codes as packed 16-bit pairs; bf16 pairs carry a +128 offset that is removed below
-        uint32_t cp[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t a = (ko >> (6 * e)) & 7u, bb = (ko >> (6 * e + 3)) & 7u;
-          if constexpr (BF16) {
-            cp[e] = (a | (bb << 16)) | 0x43004300u;              // 128 + code
-          } else {
-            const uint32_t magic = (a | (bb << 16)) | 0x64006400u;  // 1024 + code
-            const f16x2_t v = __builtin_bit_cast(f16x2_t, magic) - (f16x2_t){1024.0f16, 1024.0f16};
-            cp[e] = __builtin_bit_cast(uint32_t, v);
-          }
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float d = 0.f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) d = dot2<BF16>(qv[g][e], cp[e], d);
-          d = group_sum<LPR>(d);
-          const float off = BF16 ? 128.f + kz : kz;
-          sc[i][g] = valid[i] ? ks * (d - off * qsum[g]) * p.scale_log2 : neg_inf();
-        }
-        const uint32_t vo = __builtin_amdgcn_alignbit(vhi[i], vlo[i], sh) & 0xffffffu;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vf[i][e] = (float)((vo >> (3 * e)) & 7u);
-        vs[i] = valid[i] ? f16_lo(vmeta[i]) : 0.f;
-        vz[i] = valid[i] ? f16_hi(vmeta[i]) : 0.f;
-      }
+    for (int i = 0; i < Gm::NI; ++i) {
+      R.k[i] = *reinterpret_cast<const uint4*>(kb + o.row[i]);
+      R.v[i] = *reinterpret_cast<const uint4*>(vb + o.row[i]);
     }
-
-    // online softmax update of each row's state
-    float pp[NI][G];
+  } else {
+    // 3-bit rows: D*3/32 words; lane c owns octet c = stream bits [24c, 24c + 24), which
+    // start in word 3c/4 and spill into the next word for c mod 4 in {1, 2}.
+    const bool two = ((c & 3) == 1) || ((c & 3) == 2);
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mx = sc[0][g];
-#pragma unroll
-      for (int i = 1; i < NI; ++i) mx = fmaxf(mx, sc[i][g]);
-      const float mn = fmaxf(m[g], mx);
-      const float mu = (mn == neg_inf()) ? 0.f : mn;
-      const float al = fast_exp2(m[g] - mu);
-      m[g] = mn;
-      l[g] *= al;
-      zc[g] *= al;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[g][e] *= al;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        pp[i][g] = fast_exp2(sc[i][g] - mu);
-        l[g] += pp[i][g];
-      }
+    for (int i = 0; i < Gm::NI; ++i) {
+      R.klo[i] = *reinterpret_cast<const uint32_t*>(kb + o.row[i]);
+      R.khi[i] = two ? *reinterpret_cast<const uint32_t*>(kb + o.row[i] + 4) : 0u;
+      R.vlo[i] = *reinterpret_cast<const uint32_t*>(vb + o.row[i]);
+      R.vhi[i] = two ? *reinterpret_cast<const uint32_t*>(vb + o.row[i] + 4) : 0u;
+      R.km[i] = *reinterpret_cast<const uint32_t*>(kmb + o.meta[i]);
+      R.vm[i] = *reinterpret_cast<const uint32_t*>(vmb + o.meta[i]);
     }
+  }
+}
+
+// QK, online-softmax update and PV for one chunk of this lane's row.  MASKED: tokens at or
+// past t_end are excluded (only the last chunk of a range can be ragged).
+template <int D, int G, bool BF16, CacheKind KIND, int HPI, bool MASKED>
+__device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S,
+                                              const Regs<Geo<D, HPI>::NI, KIND>& R, int tok,
+                                              int t_end, int c) {
+  using Gm = Geo<D, HPI>;
+  constexpr int NI = Gm::NI, LPR = Gm::LPR;
+  bool valid[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) valid[i] = !MASKED || (tok + i * Gm::TPI < t_end);
+  float sc[NI][G];
+  if constexpr (KIND == CacheKind::Same) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
+      const uint32_t kw[4] = {R.k[i].x, R.k[i].y, R.k[i].z, R.k[i].w};
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        float pw = pp[i][g];
-        if constexpr (KIND == CacheKind::U3) {
-          pw *= vs[i];
-          zc[g] = fmaf(pw, vz[i], zc[g]);
-        }
+        float d = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pw, vf[i][e], acc[g][e]);
+        for (int e = 0; e < 4; ++e) d = dot2<BF16>(S.qv[g][e], kw[e], d);
+        d = group_sum<LPR>(d);
+        sc[i][g] = valid[i] ? d * p.scale_log2 : neg_inf();
+      }
+    }
+  } else {
+    const int sh = (24 * c) & 31;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t ko = __builtin_amdgcn_alignbit(R.khi[i], R.klo[i], sh) & 0xffffffu;
+      const float ks = f16_lo(R.km[i]), kz = f16_hi(R.km[i]);
+      // codes as packed 16-bit pairs: fp16 exactly (1024 + c, minus 1024); bf16 pairs keep a
+      // +128 offset that is folded into the zero point below
+      uint32_t cp[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t a = (ko >> (6 * e)) & 7u, bb = (ko >> (6 * e + 3)) & 7u;
+        if constexpr (BF16) {
+          cp[e] = (a | (bb << 16)) | 0x43004300u;
+        } else {
+          const uint32_t magic = (a | (bb << 16)) | 0x64006400u;
+          const f16x2_t v = __builtin_bit_cast(f16x2_t, magic) - (f16x2_t){1024.0f16, 1024.0f16};
+          cp[e] = __builtin_bit_cast(uint32_t, v);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d = dot2<BF16>(S.qv[g][e], cp[e], d);
+        d = group_sum<LPR>(d);
+        const float off = BF16 ? 128.f + kz : kz;
+        // q.(code - z)*s = s * (q.code - z * sum(q))
+        sc[i][g] = valid[i] ? ks * (d - off * S.qsum[g]) * p.scale_log2 : neg_inf();
       }
     }
   }
+  float pp[NI][G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float mx = sc[0][g];
+#pragma unroll
+    for (int i = 1; i < NI; ++i) mx = fmaxf(mx, sc[i][g]);
+    const float mn = fmaxf(S.m[g], mx);
+    const float mu = (MASKED && mn == neg_inf()) ? 0.f : mn;   // a row with no token yet
+    const float al = fast_exp2(S.m[g] - mu);
+    S.m[g] = mn;
+    S.l[g] *= al;
+    if constexpr (KIND == CacheKind::U3) S.zc[g] *= al;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) S.acc[g][e] *= al;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      pp[i][g] = fast_exp2(sc[i][g] - mu);
+      S.l[g] += pp[i][g];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    float vf[8];
+    if constexpr (KIND == CacheKind::Same) {
+      uint32_t vw[4] = {R.v[i].x, R.v[i].y, R.v[i].z, R.v[i].w};
+      if (MASKED && !valid[i]) vw[0] = vw[1] = vw[2] = vw[3] = 0u;   // poisoned tails stay out
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vf[2 * e] = h_lo<BF16>(vw[e]);
+        vf[2 * e + 1] = h_hi<BF16>(vw[e]);
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) S.acc[g][e] = fmaf(pp[i][g], vf[e], S.acc[g][e]);
+    } else {
+      const int sh = (24 * c) & 31;
+      const uint32_t vo = __builtin_amdgcn_alignbit(R.vhi[i], R.vlo[i], sh) & 0xffffffu;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vf[e] = (float)((vo >> (3 * e)) & 7u);
+      const float vs = valid[i] ? f16_lo(R.vm[i]) : 0.f;
+      const float vz = valid[i] ? f16_hi(R.vm[i]) : 0.f;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        // sum_t p (code - z) s = sum_t (p s) code - sum_t (p s) z
+        const float pw = pp[i][g] * vs;
+        S.zc[g] = fmaf(pw, vz, S.zc[g]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) S.acc[g][e] = fmaf(pw, vf[e], S.acc[g][e]);
+      }
+    }
+  }
+}
 
+// Reduce the chunks k = stream, stream + TS, ... of tokens [t0, t1) of request b, head group hg
+// into S (this lane's row: head hh of the group, token offset tr inside a wave instruction).
+template <int D, int G, bool BF16, CacheKind KIND, int HPI>
+__device__ __forceinline__ void run_range(const DecodeParams& p, State<G>& S, int b, int hg, int t0,
+                                          int t1, int lane, int tr, int hh, int c, int stream) {
+  using Gm = Geo<D, HPI>;
+  using R = Regs<Gm::NI, KIND>;
+  constexpr int esz = KIND == CacheKind::U3 ? 4 : 2;
+  const int nk = (t1 - t0 + Gm::CT - 1) / Gm::CT;
+  const bool ragged = ((t1 - t0) % Gm::CT) != 0;
+  const int32_t* bt_row = p.block_tables + b * p.bt_sb;
+  const int h_first = hg * p.heads_per_group;
+  const LaneOffsets<D, HPI, KIND> lo = lane_offsets<D, HPI, KIND>(p, tr, hh, c);
+  const char* kc = static_cast<const char*>(p.k_cache) + (int64_t)h_first * p.c_sh * esz;
+  const char* vc = static_cast<const char*>(p.v_cache) + (int64_t)h_first * p.c_sh * esz;
+  const char* kmc = static_cast<const char*>(p.k_meta) + (int64_t)h_first * 4;
+  const char* vmc = static_cast<const char*>(p.v_meta) + (int64_t)h_first * 4;
+  for (int win = 0; win < nk; win += 64) {
+    const int n = min(64, nk - win);
+    int bt_lane = 0;
+    if (lane < n) {
+      const int e = bt_row[(t0 + (win + lane) * Gm::CT) >> p.log2_bs];
+      bt_lane = (int)min<int64_t>(max(e, 0), p.num_blocks - 1);   // out-of-range ids clamped
+    }
+    auto chunk = [&](int k, auto masked) {
+      const int tok0 = t0 + (win + k) * Gm::CT;
+      const int64_t phys = __builtin_amdgcn_readlane(bt_lane, k);
+      const int64_t slot0 = tok0 & (p.block_size - 1);
+      const int64_t rowb = (phys * p.c_sb + slot0 * p.c_ss) * esz;
+      const int64_t metab = ((phys * p.block_size + slot0) * p.num_kv_heads) * 4;
+      R regs;
+      load_chunk<D, HPI, KIND>(kc + rowb, vc + rowb, kmc + metab, vmc + metab, lo, c, regs);
+      compute_chunk<D, G, BF16, KIND, HPI, decltype(masked)::value>(p, S, regs, tok0 + tr, t1, c);
+    };
+    // the ragged last chunk of the range is peeled off so that the loop body holds only the
+    // unmasked code
+    const int n_plain = (ragged && win + n == nk) ? n - 1 : n;
+    const int ts = p.token_streams;
+    int k = (stream - win % ts + ts) % ts;
+    for (; k < n_plain; k += ts) chunk(k, std::false_type{});
+    if (n_plain < n && k == n - 1) chunk(n - 1, std::true_type{});
+  }
+}
+
+// Merge the rows of the wave that hold the same head at different token offsets (TPI > 1).
+template <int D, int G, CacheKind KIND, int HPI>
+__device__ __forceinline__ void merge_rows(State<G>& S) {
+  using Gm = Geo<D, HPI>;
   if constexpr (KIND == CacheKind::U3) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[g][e] -= zc[g];
+      for (int e = 0; e < 8; ++e) S.acc[g][e] -= S.zc[g];
   }
-
-  // merge the token rows of this wave (lanes c, c + LPR, c + 2*LPR, ...)
 #pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) {
+  for (int off = HPI * Gm::LPR; off < 64; off <<= 1) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float mo = __shfl_xor(m[g], off);
-      const float lo = __shfl_xor(l[g], off);
-      float mn, fs, fo;
-      lse_factors(m[g], mo, mn, fs, fo);
-      l[g] = l[g] * fs + lo * fo;
+      const float mo = __shfl_xor(S.m[g], off);
+      const float lo = __shfl_xor(S.l[g], off);
+      const float mn = fmaxf(S.m[g], mo);
+      const float mu = (mn == neg_inf()) ? 0.f : mn;
+      const float fs = fast_exp2(S.m[g] - mu), fo = fast_exp2(mo - mu);
+      S.l[g] = S.l[g] * fs + lo * fo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float ao = __shfl_xor(acc[g][e], off);
-        acc[g][e] = acc[g][e] * fs + ao * fo;
+        const float ao = __shfl_xor(S.acc[g][e], off);
+        S.acc[g][e] = S.acc[g][e] * fs + ao * fo;
       }
-      m[g] = mn;
-    }
-  }
-  if (r == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sm_acc[w][g][c * 8 + e] = acc[g][e];
-      if (c == 0) {
-        sm_m[w][g] = m[g];
-        sm_l[w][g] = l[g];
-      }
-    }
-  }
-  __syncthreads();
-
-  // merge the waves; write the output (single partition) or this partition's state
-  for (int i = threadIdx.x; i < G * D; i += kWaves * 64) {
-    const int g = i / D, d = i % D;
-    float M = sm_m[0][g];
-#pragma unroll
-    for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sm_m[ww][g]);
-    const float mu = (M == neg_inf()) ? 0.f : M;
-    float L = 0.f, A = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      const float f = fast_exp2(sm_m[ww][g] - mu);
-      L += sm_l[ww][g] * f;
-      A += sm_acc[ww][g][d] * f;
-    }
-    const int h = h0 + g;
-    if (nparts == 1) {
-      const float o = A / L;
-      static_cast<uint16_t*>(p.out)[b * p.o_sb + (int64_t)h * p.o_sh + d] =
-          (uint16_t)(BF16 ? f32_to_bf16_bits(o) : f32_to_f16_bits(o));
-    } else {
-      const int64_t slot = ((int64_t)b * p.num_q_heads + h) * p.max_parts + part;
-      p.ws_acc[slot * D + d] = A;
-      if (d == 0) {
-        p.ws_ml[slot * 2] = M;
-        p.ws_ml[slot * 2 + 1] = L;
-      }
+      S.m[g] = mn;
     }
   }
 }
 
-// Log-sum-exp merge of the partitions of each (request, query head); one thread per
-// output element.  Requests that fit in one partition were written by the decode kernel.
-template <int D, bool BF16>
-__global__ __launch_bounds__(D) void merge_kernel(DecodeParams p) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  const int ctx = min(max(p.context_lens[b], 0), p.max_context_len);
-  const int nparts = (ctx + p.partition_size - 1) / p.partition_size;
-  if (nparts <= 1) return;
-  const int64_t base = ((int64_t)b * p.num_q_heads + h) * p.max_parts;
-  float M = neg_inf();
-  for (int i = 0; i < nparts; ++i) M = fmaxf(M, p.ws_ml[(base + i) * 2]);
-  float L = 0.f, A = 0.f;
-  for (int i = 0; i < nparts; ++i) {
-    const float f = fast_exp2(p.ws_ml[(base + i) * 2] - M);
-    L += p.ws_ml[(base + i) * 2 + 1] * f;
-    A += p.ws_acc[(base + i) * D + d] * f;
+// s_pref[i] = granules of requests 0..i-1 (i = 0..B), from the (clamped) context lengths.
+__device__ void build_prefix(const DecodeParams& p, int* s_pref, int* s_tile) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nwv = blockDim.x >> 6;
+  int carry = 0;
+  for (int base = 0; base < p.batch; base += blockDim.x) {
+    const int i = base + threadIdx.x;
+    int x = 0;
+    if (i < p.batch) x = (clamp_ctx(p, i) + p.partition_size - 1) / p.partition_size;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) s_tile[w] = x;
+    __syncthreads();
+    int before = carry, total = carry;
+    for (int j = 0; j < nwv; ++j) {
+      if (j < w) before += s_tile[j];
+      total += s_tile[j];
+    }
+    if (i < p.batch) s_pref[i + 1] = before + x;
+    carry = total;
+    __syncthreads();
   }
-  const float o = A / L;
-  static_cast<uint16_t*>(p.out)[b * p.o_sb + (int64_t)h * p.o_sh + d] =
-      (uint16_t)(BF16 ? f32_to_bf16_bits(o) : f32_to_f16_bits(o));
+  if (threadIdx.x == 0) s_pref[0] = 0;
+  __syncthreads();
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_out_row(const DecodeParams& p, int b, int h, int c,
+                                              const float (&a)[8], float inv_l) {
+  uint4 o;
+  o.x = pack2<BF16>(a[0] * inv_l, a[1] * inv_l);
+  o.y = pack2<BF16>(a[2] * inv_l, a[3] * inv_l);
+  o.z = pack2<BF16>(a[4] * inv_l, a[5] * inv_l);
+  o.w = pack2<BF16>(a[6] * inv_l, a[7] * inv_l);
+  *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + b * p.o_sb + (int64_t)h * p.o_sh + c * 8) = o;
+}
+
+template <int D, int G, bool BF16, CacheKind KIND, int HPI>
+__global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) {
+  using Gm = Geo<D, HPI>;
+  extern __shared__ int s_pref[];              // batch + 1 entries
+  __shared__ int s_tile[kMaxWaves];
+  build_prefix(p, s_pref, s_tile);
+  if (blockIdx.x == 0)                         // the merge kernel reads the same prefix
+    for (int i = threadIdx.x; i <= p.batch; i += blockDim.x) p.ws_prefix[i] = s_pref[i];
+
+  const int lane = threadIdx.x & 63;
+  const int hw_count = p.heads_per_group / HPI;  // waves per token stream
+  const int wv = (threadIdx.x >> 6) % hw_count;  // wave inside the token stream
+  const int stream = (threadIdx.x >> 6) / hw_count;
+  const int r = lane / Gm::LPR;
+  const int c = lane % Gm::LPR;
+  const int hr = r % HPI;                       // head of the row inside the instruction
+  const int tr = r / HPI;                       // token offset of the row
+  // token streams 1.. hand their per-segment state to stream 0 through LDS:
+  // [stream - 1][head in group][query head][D accumulators, m, l]
+  float* s_x = reinterpret_cast<float*>(s_pref + ((p.batch + 1 + 3) & ~3));
+  const int64_t NHG = p.num_head_groups;
+  const int64_t total = NHG * s_pref[p.batch];            // units of all segments
+  const int64_t nwg = p.num_wgs;
+  const int64_t wg = blockIdx.x;
+  int64_t x = wg * total / nwg;
+  const int64_t x_end = (wg + 1) * total / nwg;
+  bool first = true;
+  while (x < x_end) {
+    // segment (request b, head group hg) holding unit x: the last b with NHG*s_pref[b] <= x
+    int lo = 0, hi = p.batch;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (NHG * s_pref[mid] <= x) lo = mid; else hi = mid;
+    }
+    const int b = lo;
+    const int n = s_pref[b + 1] - s_pref[b];
+    const int64_t off = x - NHG * s_pref[b];
+    const int hg = (int)(off / n);
+    const int g0 = (int)(off - (int64_t)hg * n);
+    const int g1 = (int)min<int64_t>(n, g0 + (x_end - x));
+    const int ctx = clamp_ctx(p, b);
+    const int t0 = g0 * p.partition_size;
+    const int t1 = min(ctx, g1 * p.partition_size);
+    const int hh = wv * HPI + hr;                          // head inside the group
+    const int h = hg * p.heads_per_group + hh;             // kv head of this lane's row
+
+    State<G> S;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) +
+                                                      b * p.q_sb + (int64_t)(h * G + g) * p.q_sh + c * 8);
+      S.qv[g][0] = v.x; S.qv[g][1] = v.y; S.qv[g][2] = v.z; S.qv[g][3] = v.w;
+      S.qsum[g] = 0.f;
+      if constexpr (KIND == CacheKind::U3) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s += h_lo<BF16>(S.qv[g][e]) + h_hi<BF16>(S.qv[g][e]);
+        S.qsum[g] = group_sum<Gm::LPR>(s);
+      }
+      S.m[g] = neg_inf();
+      S.l[g] = 0.f;
+      S.zc[g] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) S.acc[g][e] = 0.f;
+    }
+    run_range<D, G, BF16, KIND, HPI>(p, S, b, hg, t0, t1, lane, tr, hh, c, stream);
+    merge_rows<D, G, KIND, HPI>(S);
+    if (p.token_streams > 1) {
+      if (stream > 0 && tr == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float* xs = s_x + (((int64_t)(stream - 1) * p.heads_per_group + hh) * G + g) * (D + 2);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xs[c * 8 + e] = S.acc[g][e];
+          if (c == 0) {
+            xs[D] = S.m[g];
+            xs[D + 1] = S.l[g];
+          }
+        }
+      }
+      __syncthreads();
+      if (stream == 0) {
+        for (int q = 1; q < p.token_streams; ++q) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float* xs = s_x + (((int64_t)(q - 1) * p.heads_per_group + hh) * G + g) * (D + 2);
+            const float mo = xs[D], lo2 = xs[D + 1];
+            const float mn = fmaxf(S.m[g], mo);
+            const float mu = (mn == neg_inf()) ? 0.f : mn;
+            const float fs = fast_exp2(S.m[g] - mu), fo = fast_exp2(mo - mu);
+            S.l[g] = S.l[g] * fs + lo2 * fo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) S.acc[g][e] = S.acc[g][e] * fs + xs[c * 8 + e] * fo;
+            S.m[g] = mn;
+          }
+        }
+      }
+      __syncthreads();                          // the buffer is reused by the next segment
+    }
+    if (stream == 0 && tr == 0) {
+      if (g0 == 0 && g1 == n) {                   // whole segment: final output
+#pragma unroll
+        for (int g = 0; g < G; ++g) store_out_row<BF16>(p, b, h * G + g, c, S.acc[g], 1.f / S.l[g]);
+      } else {                                    // part of a split segment
+        const int64_t slot = (wg * 2 + (first ? 0 : 1)) * p.heads_per_group + hh;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float* dst = p.ws_acc + (slot * G + g) * D + c * 8;
+          *reinterpret_cast<float4*>(dst) = make_float4(S.acc[g][0], S.acc[g][1], S.acc[g][2], S.acc[g][3]);
+          *reinterpret_cast<float4*>(dst + 4) = make_float4(S.acc[g][4], S.acc[g][5], S.acc[g][6], S.acc[g][7]);
+          if (c == 0) *reinterpret_cast<float2*>(p.ws_ml + (slot * G + g) * 2) = make_float2(S.m[g], S.l[g]);
+        }
+      }
+    }
+    x += g1 - g0;
+    first = false;
+  }
+}
+
+// One workgroup per (request, kv head, query head of the group): merges the partial states
+// of a split segment by log-sum-exp, writes zeros for an empty context, and leaves
+// single-workgroup segments alone.  The D x kMergeSplit threads split the partials
+// kMergeSplit ways (each with kMergeBatch loads in flight), then combine through LDS.
+constexpr int kMergeSplit = 4;
+constexpr int kMergeBatch = 4;
+
+template <int D, int G, bool BF16>
+__global__ __launch_bounds__(D * kMergeSplit) void merge_kernel(DecodeParams p) {
+  __shared__ float s_m[kMergeSplit][D], s_l[kMergeSplit][D], s_a[kMergeSplit][D];
+  const int g = blockIdx.x % G;
+  const int kvh = (blockIdx.x / G) % p.num_kv_heads;
+  const int b = blockIdx.x / (G * p.num_kv_heads);
+  const int hg = kvh / p.heads_per_group, hh = kvh % p.heads_per_group;
+  const int d = threadIdx.x % D, part = threadIdx.x / D;
+  const int64_t NHG = p.num_head_groups;
+  const int pb = p.ws_prefix[b], n = p.ws_prefix[b + 1] - pb;
+  uint16_t* out = static_cast<uint16_t*>(p.out) + b * p.o_sb + (int64_t)(kvh * G + g) * p.o_sh;
+  if (n == 0) {
+    if (part == 0) out[d] = 0;
+    return;
+  }
+  const int64_t total = NHG * p.ws_prefix[p.batch];
+  const int64_t nwg = p.num_wgs;
+  const int64_t s0 = NHG * pb + (int64_t)hg * n, s1 = s0 + n - 1;
+  const int64_t w0 = ((s0 + 1) * nwg - 1) / total;     // workgroup that owns unit s0
+  const int64_t w1 = ((s1 + 1) * nwg - 1) / total;
+  if (w0 == w1) return;                                // one workgroup covered it and wrote out
+  // Partials: workgroup w0 holds the segment's head in slot 0 if the segment starts its range,
+  // else in slot 1; workgroups w0+1 .. w1 hold the rest in slot 0.  With fewer units than
+  // workgroups some ranges are empty and those workgroups wrote nothing.
+  const bool maybe_empty = total < nwg;
+  const int64_t hpg = p.heads_per_group;
+  auto slot_of = [&](int64_t j) {        // j-th partial, j = 0 .. w1 - w0
+    const int64_t w = w0 + j;
+    const int s = (j == 0 && w0 * total / nwg != s0) ? 1 : 0;
+    return ((w * 2 + s) * hpg + hh) * G + g;
+  };
+  auto live = [&](int64_t j) {
+    if (j > w1 - w0) return false;
+    if (!maybe_empty || j == 0) return true;
+    const int64_t w = w0 + j;
+    return w * total / nwg < (w + 1) * total / nwg;
+  };
+  float M = neg_inf(), L = 0.f, A = 0.f;
+  for (int64_t j0 = part; j0 <= w1 - w0; j0 += kMergeSplit * kMergeBatch) {
+    float2 ml[kMergeBatch];
+    float a[kMergeBatch];
+    bool ok[kMergeBatch];
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {            // independent loads, all in flight
+      const int64_t j = j0 + (int64_t)u * kMergeSplit;
+      ok[u] = live(j);
+      const int64_t sl = ok[u] ? slot_of(j) : 0;
+      ml[u] = ok[u] ? *reinterpret_cast<const float2*>(p.ws_ml + sl * 2) : make_float2(neg_inf(), 0.f);
+      a[u] = ok[u] ? p.ws_acc[sl * D + d] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeBatch; ++u) {
+      if (!ok[u]) continue;
+      const float mn = fmaxf(M, ml[u].x);              // partial maxima are finite
+      const float fo = fast_exp2(M - mn), fn = fast_exp2(ml[u].x - mn);
+      L = L * fo + ml[u].y * fn;
+      A = A * fo + a[u] * fn;
+      M = mn;
+    }
+  }
+  s_m[part][d] = M;
+  s_l[part][d] = L;
+  s_a[part][d] = A;
+  __syncthreads();
+  if (part == 0) {
+    float Mt = s_m[0][d];
+#pragma unroll
+    for (int q = 1; q < kMergeSplit; ++q) Mt = fmaxf(Mt, s_m[q][d]);
+    float Lt = 0.f, At = 0.f;
+#pragma unroll
+    for (int q = 0; q < kMergeSplit; ++q) {
+      const float f = fast_exp2(s_m[q][d] - Mt);       // an empty split has m = -inf, f = 0
+      Lt += s_l[q][d] * f;
+      At += s_a[q][d] * f;
+    }
+    const float o = At / Lt;
+    out[d] = (uint16_t)(BF16 ? f32_to_bf16_bits(o) : f32_to_f16_bits(o));
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Host side: geometry, occupancy-sized grid, dispatch.
+// ---------------------------------------------------------------------------------------
+namespace {
+
+int heads_per_instr(int head_dim, int num_kv_heads) {
+  const int rpi = 64 / (head_dim / 8);
+  int hpi = 1;
+  while (hpi * 2 <= rpi && num_kv_heads % (hpi * 2) == 0) hpi *= 2;
+  return hpi;
+}
+
+template <int D, int G, bool BF16, CacheKind KIND, int HPI>
+const void* kernel_ptr() {
+  return reinterpret_cast<const void*>(&decode_kernel<D, G, BF16, KIND, HPI>);
 }
 
 template <int D, int G, bool BF16, CacheKind KIND>
-static hipError_t launch_t(const DecodeParams& p, int batch, hipStream_t s) {
-  const int64_t wgs = (int64_t)p.max_parts * p.num_kv_heads * batch;
-  hipLaunchKernelGGL((decode_kernel<D, G, BF16, KIND>), dim3((unsigned)wgs), dim3(kWaves * 64), 0, s,
-                     p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.max_parts <= 1) return e;
-  hipLaunchKernelGGL((merge_kernel<D, BF16>), dim3((unsigned)p.num_q_heads, (unsigned)batch),
-                     dim3(D), 0, s, p);
-  return hipGetLastError();
-}
-
-template <int D, int G, bool BF16>
-static hipError_t by_kind(const DecodeParams& p, CacheKind kind, int batch, hipStream_t s) {
-  if (kind == CacheKind::U3) return launch_t<D, G, BF16, CacheKind::U3>(p, batch, s);
-  return launch_t<D, G, BF16, CacheKind::Same>(p, batch, s);
-}
-
-template <int D, bool BF16>
-static hipError_t by_group(const DecodeParams& p, CacheKind kind, int group, int batch,
-                           hipStream_t s) {
-  switch (group) {
-    case 1: return by_kind<D, 1, BF16>(p, kind, batch, s);
-    case 2: return by_kind<D, 2, BF16>(p, kind, batch, s);
-    case 4: return by_kind<D, 4, BF16>(p, kind, batch, s);
-    case 8: return by_kind<D, 8, BF16>(p, kind, batch, s);
+const void* kernel_by_hpi(int hpi) {
+  switch (hpi) {
+    case 1: return kernel_ptr<D, G, BF16, KIND, 1>();
+    case 2: return kernel_ptr<D, G, BF16, KIND, 2>();
+    case 4: return kernel_ptr<D, G, BF16, KIND, 4>();
+    case 8: if constexpr (D == 64) return kernel_ptr<D, G, BF16, KIND, 8>(); else return nullptr;
   }
-  return hipErrorInvalidValue;
+  return nullptr;
 }
 
-hipError_t launch_decode(const DecodeParams& p, CacheKind kind, bool bf16, int head_dim, int group,
-                         int batch, hipStream_t s) {
-  if (batch == 0) return hipSuccess;
-  if (head_dim == 128)
-    return bf16 ? by_group<128, true>(p, kind, group, batch, s)
-                : by_group<128, false>(p, kind, group, batch, s);
-  return bf16 ? by_group<64, true>(p, kind, group, batch, s)
-              : by_group<64, false>(p, kind, group, batch, s);
+template <int D, bool BF16, CacheKind KIND>
+const void* kernel_by_g(int group, int hpi) {
+  switch (group) {
+    case 1: return kernel_by_hpi<D, 1, BF16, KIND>(hpi);
+    case 2: return kernel_by_hpi<D, 2, BF16, KIND>(hpi);
+    case 4: return kernel_by_hpi<D, 4, BF16, KIND>(hpi);
+    case 8: return kernel_by_hpi<D, 8, BF16, KIND>(hpi);
+  }
+  return nullptr;
 }
 
-int auto_partition_size(int max_context_len, int batch, int num_q_heads) {
-  (void)max_context_len;
-  (void)batch;
-  (void)num_q_heads;
-  return 512;
+const void* decode_kernel_ptr(int head_dim, int group, bool bf16, CacheKind kind, int hpi) {
+  if (head_dim == 128) {
+    if (kind == CacheKind::U3)
+      return bf16 ? kernel_by_g<128, true, CacheKind::U3>(group, hpi) : kernel_by_g<128, false, CacheKind::U3>(group, hpi);
+    return bf16 ? kernel_by_g<128, true, CacheKind::Same>(group, hpi) : kernel_by_g<128, false, CacheKind::Same>(group, hpi);
+  }
+  if (kind == CacheKind::U3)
+    return bf16 ? kernel_by_g<64, true, CacheKind::U3>(group, hpi) : kernel_by_g<64, false, CacheKind::U3>(group, hpi);
+  return bf16 ? kernel_by_g<64, true, CacheKind::Same>(group, hpi) : kernel_by_g<64, false, CacheKind::Same>(group, hpi);
 }
+
+const void* merge_kernel_ptr(int head_dim, int group, bool bf16) {
+#define PKV_MERGE(DD, GG)                                                                   \
+  if (head_dim == DD && group == GG)                                                        \
+    return bf16 ? reinterpret_cast<const void*>(&merge_kernel<DD, GG, true>)               \
+                : reinterpret_cast<const void*>(&merge_kernel<DD, GG, false>);
+  PKV_MERGE(128, 1) PKV_MERGE(128, 2) PKV_MERGE(128, 4) PKV_MERGE(128, 8)
+  PKV_MERGE(64, 1) PKV_MERGE(64, 2) PKV_MERGE(64, 4) PKV_MERGE(64, 8)
+#undef PKV_MERGE
+  return nullptr;
+}
+
+int resident_wgs_per_cu(const void* fn, int threads, size_t lds) {
+  int n = 0;
+  if (!fn || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, lds) != hipSuccess || n <= 0)
+    n = 8;                         // no device to ask: assume the most a CU can hold
+  return n;
+}
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  return cus;
+}
+
+}  // namespace
+
+DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int head_dim, int max_context_len,
+                       int partition_size, int bf16, int kind) {
+  DecodePlan P{};
+  P.hpi = heads_per_instr(head_dim, num_kv_heads);
+  const int waves = num_kv_heads / P.hpi;        // waves to cover all heads of a token
+  int hw = 1;                                    // head waves per workgroup (at most 4)
+  for (int w = std::min(waves, 4); w >= 1; --w)
+    if (waves % w == 0) { hw = w; break; }
+  P.token_streams = (2 * hw <= kMaxWaves) ? 2 : 1;
+  P.waves_per_wg = hw * P.token_streams;
+  P.heads_per_group = P.hpi * hw;
+  P.num_head_groups = num_kv_heads / P.heads_per_group;
+  const int group = num_q_heads / num_kv_heads;
+  P.lds_bytes = (size_t)((batch + 1 + 3) & ~3) * sizeof(int) +
+                (size_t)(P.token_streams - 1) * P.heads_per_group * group * (head_dim + 2) * sizeof(float);
+  int per_cu = 0;
+  for (int bf = 0; bf < 2; ++bf)
+    for (int kd = 0; kd < 2; ++kd) {
+      if ((bf16 >= 0 && bf != bf16) || (kind >= 0 && kd != kind)) continue;
+      const CacheKind ck = kd ? CacheKind::U3 : CacheKind::Same;
+      per_cu = std::max(per_cu, resident_wgs_per_cu(decode_kernel_ptr(head_dim, group, bf != 0, ck, P.hpi),
+                                                    P.waves_per_wg * 64, P.lds_bytes));
+    }
+  const int64_t units = (int64_t)batch * P.num_head_groups *
+                        ((max_context_len + partition_size - 1) / partition_size);
+  P.num_wgs = std::min<int64_t>((int64_t)device_cus() * per_cu, std::max<int64_t>(units, 1));
+  return P;
+}
+
+hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan, CacheKind kind, bool bf16,
+                         int head_dim, int group, hipStream_t s) {
+  if (p.batch == 0) return hipSuccess;
+  const void* fn = decode_kernel_ptr(head_dim, group, bf16, kind, plan.hpi);
+  const void* mf = merge_kernel_ptr(head_dim, group, bf16);
+  if (!fn || !mf) return hipErrorInvalidValue;
+  void* args[] = {const_cast<DecodeParams*>(&p)};
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)plan.num_wgs), dim3(plan.waves_per_wg * 64), args,
+                                 plan.lds_bytes, s);
+  if (e != hipSuccess) return e;
+  e = hipLaunchKernel(mf, dim3((unsigned)(p.batch * p.num_kv_heads * group)), dim3(head_dim * kMergeSplit),
+                      args, 0, s);
+  return e != hipSuccess ? e : hipGetLastError();
+}
+
+int auto_partition_size(int, int, int) { return 16; }
 
 }  // namespace pkv

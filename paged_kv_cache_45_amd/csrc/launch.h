@@ -41,11 +41,26 @@ struct DecodeParams {
   int block_size, log2_bs;
   int64_t num_blocks;                 // block-table entries are clamped into [0, num_blocks)
   int max_context_len;                // context lengths are clamped into [0, max_context_len]
-  int partition_size;                 // tokens, multiple of 16
-  int max_parts;                      // partitions per request in the grid
+  int partition_size;                 // split granule in tokens, multiple of 16
+  int64_t num_wgs;                    // workgroups in the decode grid
+  int heads_per_group;                // kv heads one workgroup covers
+  int num_head_groups;                // num_kv_heads / heads_per_group
+  int token_streams;                  // waves sets of a workgroup splitting its chunks
   float scale_log2;                   // sm_scale * log2(e)
-  float* ws_acc;                      // [B, Hq, max_parts, D] (split only)
-  float* ws_ml;                       // [B, Hq, max_parts, 2]
+  float* ws_acc;                      // [num_wgs, 2, heads_per_group, G, D] partial accumulators
+  float* ws_ml;                       // [num_wgs, 2, heads_per_group, G, 2] partial (m, l)
+  int* ws_prefix;                     // [batch + 1] granule prefix sums
+};
+
+// Launch geometry of paged_decode.
+struct DecodePlan {
+  int hpi;                            // kv heads per wave instruction
+  int waves_per_wg;
+  int heads_per_group;                // hpi * (waves_per_wg / token_streams)
+  int num_head_groups;
+  int token_streams;                  // interleaved chunk streams per workgroup
+  int64_t num_wgs;                    // as many as stay resident, at most one per unit
+  size_t lds_bytes;                   // dynamic LDS of the decode kernel
 };
 
 hipError_t launch_pack3(const uint8_t* values, uint8_t* packed, int64_t n_values, hipStream_t s);
@@ -55,10 +70,15 @@ hipError_t launch_unpack3(const uint8_t* packed, uint8_t* values, int64_t n_valu
 hipError_t launch_append(const AppendParams& p, CacheKind kind, bool bf16, int head_dim,
                          hipStream_t s);
 
-hipError_t launch_decode(const DecodeParams& p, CacheKind kind, bool bf16, int head_dim, int group,
-                         int batch, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan, CacheKind kind, bool bf16,
+                         int head_dim, int group, hipStream_t s);
 
-// Split-K partition size used when the caller passes 0.
+// Split granule used when the caller passes 0.
 int auto_partition_size(int max_context_len, int batch, int num_q_heads);
+
+// Launch geometry on the current device; bf16 / kind = -1 plans for the largest grid any
+// dtype or cache kind would use (for sizing a workspace).
+DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int head_dim, int max_context_len,
+                       int partition_size, int bf16, int kind);
 
 }  // namespace pkv

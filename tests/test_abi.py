@@ -81,7 +81,8 @@ def _decode(lib, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(out=None), -1), (dict(bt=None), -1), (dict(Hq=24, Hkv=8), -2), (dict(Hq=30), -1),
     (dict(Hq=128, Hkv=8), -2), (dict(D=256), -2), (dict(bs=48), -1), (dict(cdt=2), -2),
-    (dict(qdt=0), -1), (dict(bts=100), -1), (dict(ps=24), -1), (dict(ps=8192), -2),
+    (dict(qdt=0), -1), (dict(bts=100), -1), (dict(ps=24), -1), (dict(ps=1 << 21), -2),
+    (dict(B=9000, bts=257), -2),
     (dict(ws=None), -3), (dict(wsb=100), -3), (dict(scale=float("nan")), -1),
     (dict(q=FAKE8), -1), (dict(B=-1), -1), (dict(maxctx=-5), -1), (dict(cdt=3), -1),
 ])
@@ -94,11 +95,16 @@ def test_decode_batch_zero_is_ok_without_launch(lib):
 
 
 def test_workspace_size(lib):
-    assert P.paged_decode_workspace_size(64, 32, 128, 512, 512) == 0
-    n = P.paged_decode_workspace_size(64, 32, 128, 4097, 512)
-    assert n == 64 * 32 * 9 * 130 * 4
-    with pytest.raises(ValueError):
-        P.paged_decode_workspace_size(64, 32, 128, 4097, 24)
+    assert P.paged_decode_workspace_size(0, 32, 8, 128, 512, 0) == 0
+    n = P.paged_decode_workspace_size(64, 32, 8, 128, 4097, 0)
+    # partials of at most (256 CUs x 8) workgroups x 2 slots x 8 kv heads x G=4 query heads
+    # x (D + 2) floats, plus the prefix sums (each part 256-byte aligned)
+    assert 0 < n <= 2048 * 2 * 8 * 4 * 130 * 4 + 3 * 256 + 65 * 4
+    small = P.paged_decode_workspace_size(2, 4, 4, 64, 26, 0)
+    assert 0 < small < n
+    for bad in [(64, 32, 8, 128, 4097, 24), (64, 30, 8, 128, 4097, 0), (9000, 32, 8, 128, 10, 0)]:
+        with pytest.raises(ValueError):
+            P.paged_decode_workspace_size(*bad)
 
 
 def test_pack_validation(lib):

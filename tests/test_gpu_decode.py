@@ -74,7 +74,7 @@ def test_llama8b_full_size_all_heads():
     assert report("llama8b", f32_of(out), want, wl.dtype) <= ATTN_TOL
 
 
-@pytest.mark.parametrize("ps", [0, 16, 256, 4096])
+@pytest.mark.parametrize("ps", [0, 16, 256, 512, 4096])
 def test_partition_sizes_agree(ps):
     P = need_gpu()
     wl = W.llama8b_decode("cuda", batch=6)
