@@ -30,7 +30,8 @@
 //    each row keeps its own online-softmax state (m, l in log2 units, the lane's 8
 //    accumulator columns per query head).
 //  * Physical block ids of up to 64 chunks are fetched with one vector load (lane k <->
-//    k-th chunk) and read back with v_readlane.
+//    k-th chunk) and read back with v_readlane; the next chunk's K/V loads are issued before
+//    the current chunk is computed (two register buffers).
 #include <algorithm>
 #include <type_traits>
 
@@ -261,23 +262,42 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, State<G>& S, in
       const int e = bt_row[(t0 + (win + lane) * Gm::CT) >> p.log2_bs];
       bt_lane = (int)min<int64_t>(max(e, 0), p.num_blocks - 1);   // out-of-range ids clamped
     }
-    auto chunk = [&](int k, auto masked) {
+    auto issue = [&](int k, R& regs) {
       const int tok0 = t0 + (win + k) * Gm::CT;
       const int64_t phys = __builtin_amdgcn_readlane(bt_lane, k);
       const int64_t slot0 = tok0 & (p.block_size - 1);
       const int64_t rowb = (phys * p.c_sb + slot0 * p.c_ss) * esz;
       const int64_t metab = ((phys * p.block_size + slot0) * p.num_kv_heads) * 4;
-      R regs;
       load_chunk<D, HPI, KIND>(kc + rowb, vc + rowb, kmc + metab, vmc + metab, lo, c, regs);
-      compute_chunk<D, G, BF16, KIND, HPI, decltype(masked)::value>(p, S, regs, tok0 + tr, t1, c);
     };
-    // the ragged last chunk of the range is peeled off so that the loop body holds only the
-    // unmasked code
-    const int n_plain = (ragged && win + n == nk) ? n - 1 : n;
+    auto tok_of = [&](int k) { return t0 + (win + k) * Gm::CT + tr; };
+    // this stream's chunks k = first, first + ts, ... of the window; the ragged last chunk of
+    // the range is peeled off so that the loop body holds only the unmasked code, and the
+    // next chunk's loads are always in flight while the current one is computed
     const int ts = p.token_streams;
+    const int n_plain = (ragged && win + n == nk) ? n - 1 : n;
     int k = (stream - win % ts + ts) % ts;
-    for (; k < n_plain; k += ts) chunk(k, std::false_type{});
-    if (n_plain < n && k == n - 1) chunk(n - 1, std::true_type{});
+    if (k < n_plain) {
+      R ra, rb;
+      issue(k, ra);
+      for (;;) {
+        const int k1 = k + ts;
+        if (k1 < n_plain) issue(k1, rb);
+        compute_chunk<D, G, BF16, KIND, HPI, false>(p, S, ra, tok_of(k), t1, c);
+        k = k1;
+        if (k >= n_plain) break;
+        const int k2 = k + ts;
+        if (k2 < n_plain) issue(k2, ra);
+        compute_chunk<D, G, BF16, KIND, HPI, false>(p, S, rb, tok_of(k), t1, c);
+        k = k2;
+        if (k >= n_plain) break;
+      }
+    }
+    if (n_plain < n && k == n - 1) {
+      R regs;
+      issue(n - 1, regs);
+      compute_chunk<D, G, BF16, KIND, HPI, true>(p, S, regs, tok_of(n - 1), t1, c);
+    }
   }
 }
 
@@ -471,14 +491,15 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
 
 // One workgroup per (request, kv head, query head of the group): merges the partial states
 // of a split segment by log-sum-exp, writes zeros for an empty context, and leaves
-// single-workgroup segments alone.  The D x kMergeSplit threads split the partials
-// kMergeSplit ways (each with kMergeBatch loads in flight), then combine through LDS.
-constexpr int kMergeSplit = 4;
+// single-workgroup segments alone.  The D x splits threads split the partials `splits` ways
+// (each with kMergeBatch loads in flight), then combine through LDS.
+constexpr int kMergeMaxSplit = 8;
 constexpr int kMergeBatch = 4;
 
 template <int D, int G, bool BF16>
-__global__ __launch_bounds__(D * kMergeSplit) void merge_kernel(DecodeParams p) {
-  __shared__ float s_m[kMergeSplit][D], s_l[kMergeSplit][D], s_a[kMergeSplit][D];
+__global__ __launch_bounds__(D * kMergeMaxSplit) void merge_kernel(DecodeParams p) {
+  __shared__ float s_m[kMergeMaxSplit][D], s_l[kMergeMaxSplit][D], s_a[kMergeMaxSplit][D];
+  const int kMergeSplit = blockDim.x / D;
   const int g = blockIdx.x % G;
   const int kvh = (blockIdx.x / G) % p.num_kv_heads;
   const int b = blockIdx.x / (G * p.num_kv_heads);
@@ -542,10 +563,8 @@ __global__ __launch_bounds__(D * kMergeSplit) void merge_kernel(DecodeParams p) 
   __syncthreads();
   if (part == 0) {
     float Mt = s_m[0][d];
-#pragma unroll
     for (int q = 1; q < kMergeSplit; ++q) Mt = fmaxf(Mt, s_m[q][d]);
     float Lt = 0.f, At = 0.f;
-#pragma unroll
     for (int q = 0; q < kMergeSplit; ++q) {
       const float f = fast_exp2(s_m[q][d] - Mt);       // an empty split has m = -inf, f = 0
       Lt += s_l[q][d] * f;
@@ -673,7 +692,11 @@ hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan, CacheKin
   hipError_t e = hipLaunchKernel(fn, dim3((unsigned)plan.num_wgs), dim3(plan.waves_per_wg * 64), args,
                                  plan.lds_bytes, s);
   if (e != hipSuccess) return e;
-  e = hipLaunchKernel(mf, dim3((unsigned)(p.batch * p.num_kv_heads * group)), dim3(head_dim * kMergeSplit),
+  // split the partials of a segment so that each thread merges about 2 x kMergeBatch of them
+  const int64_t per_seg = plan.num_wgs / std::max<int64_t>(1, (int64_t)p.batch * plan.num_head_groups) + 2;
+  int splits = 1;
+  while (splits < kMergeMaxSplit && per_seg > (int64_t)splits * 2 * kMergeBatch) splits *= 2;
+  e = hipLaunchKernel(mf, dim3((unsigned)(p.batch * p.num_kv_heads * group)), dim3(head_dim * splits),
                       args, 0, s);
   return e != hipSuccess ? e : hipGetLastError();
 }
