@@ -1,10 +1,10 @@
 """Benchmark of the paged KV-cache hot path on one MI355X.
 
-One step = the whole path over one Llama-8B-shaped decode batch: kv_append of one new
-token per request (64 tokens, bf16, 8 kv heads of 128) into a paged pool (block size 16),
-then paged_decode of one query token per request (32 q heads, GQA 4) over the updated
-context (513..4097 tokens, U{512..4096} cached + 1), split-K partitions merged by
-log-sum-exp.  Inputs are synthetic, seeded, already resident in HBM.
+Default workload (the headline): one step = the whole path over one Llama-8B-shaped decode
+batch: kv_append of one new token per request (64 tokens, bf16, 8 kv heads of 128) into a
+paged pool (block size 16), then paged_decode of one query token per request (32 q heads,
+GQA 4) over the updated context (513..4097 tokens, U{512..4096} cached + 1), split-K
+ranges merged by log-sum-exp.  Inputs are synthetic, seeded, already resident in HBM.
 
 Four per-layer pools (same shapes and block tables, different data) are used in rotation,
 one per step, as in a multi-layer decode: between two reads of a pool ~1.8 GB of other
@@ -12,13 +12,25 @@ KV data is read, so the 256 MB Infinity Cache cannot hold it and the timed reads
 from HBM.
 
 Prints ONE JSON line.  value = algorithmic bytes of the step / step time (GB/s).
+
+Other workloads (--workload), each one JSON line of the same form, for the measurements
+of the remaining shapes:
+  mixed-append-fp8   8 prompts U{128..2048} + 56 decode tokens, 10% padding slots, bf16 ->
+                     fp8 e4m3fn cache with per-row scales, block size 32 (tokens/s)
+  long-context       B=8, 64/8 heads, block size 64, contexts U{32k..128k}, partitions of
+                     512 tokens (KV GB/s)
+  packed3-decode     B=32, 32/8 heads, 3-bit cache with fp16 (scale, zero), block size 16,
+                     contexts U{1k..16k}, fp16 query (KV GB/s)
+  pack3-exhaustive   pack3 + unpack3 over all 2^24 octets, with the bijection check
+  copy-calibration   a plain device copy of 1 GiB, the reference for HBM byte counters
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
-import math
 import os
+import re
 import sys
 import time
 
@@ -28,29 +40,131 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 N_LAYERS = 4
+METRIC = "paged decode KV GB/s (% of HBM peak) + append tokens/s, Llama-8B shape"
+DECODE_SOURCES = ("paged_kv_cache_45_amd/csrc/decode.hip", "paged_kv_cache_45_amd/csrc/common.cuh",
+                  "paged_kv_cache_45_amd/csrc/launch.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama8b_hbm_traffic.md")
+
+
+# ----------------------------------------------------------------------------------------
+# algorithmic bytes (the bytes the method must move; the same formulas are stated with the
+# kernels' roofline figures in the design notes)
+# ----------------------------------------------------------------------------------------
+def decode_bytes(wl, kv_bytes_per_token_head):
+    """K/V of every live token + q read + out written + the block-table entries used."""
+    H, D, B, Hq = wl.num_kv_heads, wl.head_dim, wl.batch, wl.num_q_heads
+    ctx = wl.ctx_after.long()
+    kv = int(ctx.sum()) * H * kv_bytes_per_token_head
+    qo = 2 * B * Hq * D * 2
+    bt = int(((ctx + wl.block_size - 1) // wl.block_size).sum()) * 4 + B * 4
+    return kv + qo + bt, kv
 
 
 def algorithmic_bytes(wl):
-    """Bytes the method must move, per step (the design doc states the same formulas)."""
-    H, D, B, Hq = wl.num_kv_heads, wl.head_dim, wl.batch, wl.num_q_heads
-    esz = 2
-    ctx = wl.ctx_after.long()
-    kv = int(ctx.sum()) * H * D * esz * 2                  # K and V rows of every live token
-    qo = 2 * B * Hq * D * esz                              # q read + out written
-    bt = int(((ctx + wl.block_size - 1) // wl.block_size).sum()) * 4 + B * 4
-    decode = kv + qo + bt
-    append = B * H * D * esz * 2 * 2 + B * 8              # read new K,V + write rows + slots
-    return decode, append, kv
+    """Llama-8B step: (decode bytes, append bytes, KV bytes)."""
+    H, D, B = wl.num_kv_heads, wl.head_dim, wl.batch
+    dec, kv = decode_bytes(wl, 2 * D * 2)
+    append = B * H * D * 2 * 2 * 2 + B * 8                # read new K,V + write rows + slots
+    return dec, append, kv
 
 
-def cpu_baseline(wl, hk_bits, hv_bits, budget_s=12.0, max_reps=5):
+def sources_sha256():
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per paged_decode launch from the committed counter summary, or None when
+    there is none or the decode sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    m = re.search(r"^traffic-record: (\{.*\})$", text, re.M)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("sources_sha256") != sources_sha256():
+        return None
+    return int(rec["hbm_bytes_per_launch"])
+
+
+def event_times_ms(fn, n, stream):
+    """Durations of n calls of fn(i), each bracketed by events on `stream`."""
+    import numpy as np
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for i in range(n):
+        ev[i][0].record(stream)
+        fn(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev])
+
+
+def graph_call_times_ms(calls, reps):
+    """Per-call durations of a short, launch-bound entry point: the calls are captured into
+    one HIP graph (they allocate nothing and record no memset) and the graph is replayed
+    `reps` times, each replay bracketed by events; returns replay time / len(calls)."""
+    import numpy as np
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):               # warm-up outside the capture
+        for c in calls:
+            c()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    stream = torch.cuda.current_stream()
+    g.replay()
+    torch.cuda.synchronize()
+    ms = event_times_ms(lambda _: g.replay(), reps, stream)
+    return ms / len(calls), g
+
+
+def stats_us(ms):
+    import numpy as np
+    return {"median": round(float(np.median(ms)) * 1e3, 2),
+            "p20_p80": [round(float(np.quantile(ms, 0.2)) * 1e3, 2),
+                        round(float(np.quantile(ms, 0.8)) * 1e3, 2)],
+            "mean": round(float(ms.mean()) * 1e3, 2)}
+
+
+def base_record(args, metric, value, unit, ms_per_step, dtype, config, higher=True):
+    return {"metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+            "higher_is_better": higher, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+            "data": "synthetic", "config": config}
+
+
+def hbm_roofline(kernel, alg_bytes, avg_s, traffic=None):
+    achieved = alg_bytes / avg_s / 1e9
+    return {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "algorithmic_bytes": int(alg_bytes)}
+
+
+# ----------------------------------------------------------------------------------------
+# the oracle baseline (host cores)
+# ----------------------------------------------------------------------------------------
+def cpu_baseline(wl, hk_bits, hv_bits, budget_s=12.0, max_reps=50):
     """The oracle as it stands, on host cores, over the same workload (append + decode)."""
     import numpy as np
+    import torch
     import oracle
     from threadpoolctl import threadpool_info
 
-    nk = wl.new_k.detach().contiguous().view(__import__("torch").int16).cpu().numpy().view(np.uint16)
-    nv = wl.new_v.detach().contiguous().view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+    nk = wl.new_k.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    nv = wl.new_v.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
     q = wl.q.float().cpu().numpy()
     slots = wl.slot_mapping.numpy()
     reps, t_total = 0, 0.0
@@ -71,33 +185,19 @@ def cpu_baseline(wl, hk_bits, hv_bits, budget_s=12.0, max_reps=5):
                       f"{reps} rep(s), {t_total:.1f} s"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--partition-size", type=int, default=0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path has no "
-              "multi-GPU component to measure.", file=sys.stderr)
-        sys.exit(2)
-
+# ----------------------------------------------------------------------------------------
+# workloads
+# ----------------------------------------------------------------------------------------
+def run_llama8b(args, P, W):
     import numpy as np
     import torch
-    import paged_kv_cache_45_amd as P
-    from paged_kv_cache_45_amd import workloads as W
-
-    torch.cuda.set_device(0)
-    P.load_library()
-    layers = []
-    for i in range(N_LAYERS):
-        wl = W.llama8b_decode("cuda", data_seed=W.BASE_SEED + 2 + 1000 * i, poison=(i == 0))
-        layers.append(wl)
+    layers = [W.llama8b_decode("cuda", data_seed=W.BASE_SEED + 2 + 1000 * i, poison=(i == 0))
+              for i in range(N_LAYERS)]
     wl0 = layers[0]
-    host_k = wl0.k_pool.contiguous().view(torch.int16).cpu().numpy().view(np.uint16).copy()
-    host_v = wl0.v_pool.contiguous().view(torch.int16).cpu().numpy().view(np.uint16).copy()
+    host_k = host_v = None
+    if not args.no_cpu_baseline:
+        host_k = wl0.k_pool.contiguous().view(torch.int16).cpu().numpy().view(np.uint16).copy()
+        host_v = wl0.v_pool.contiguous().view(torch.int16).cpu().numpy().view(np.uint16).copy()
     B, Hq, D = wl0.batch, wl0.num_q_heads, wl0.head_dim
     maxctx = max(w.max_context_len for w in layers)
     dev = [dict(bt=w.block_tables.cuda(), ctx=w.ctx_after.cuda(), slots=w.slot_mapping.cuda(),
@@ -106,17 +206,18 @@ def main():
            for w in layers]
     stream = torch.cuda.current_stream()
 
-    def step(i, ev=None):
+    def append(i):
         w, d = layers[i % N_LAYERS], dev[i % N_LAYERS]
-        if ev is not None:
-            ev[0].record(stream)
         P.kv_append(w.new_k, w.new_v, d["slots"], w.k_pool, w.v_pool)
-        if ev is not None:
-            ev[1].record(stream)
+
+    def decode(i):
+        w, d = layers[i % N_LAYERS], dev[i % N_LAYERS]
         P.paged_decode(w.q, w.k_pool, w.v_pool, d["bt"], d["ctx"], w.max_context_len, w.sm_scale,
                        partition_size=args.partition_size, workspace=d["ws"], out=d["out"])
-        if ev is not None:
-            ev[2].record(stream)
+
+    def step(i):
+        append(i)
+        decode(i)
 
     for i in range(args.warmup):
         step(i)
@@ -125,54 +226,264 @@ def main():
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
 
-    # per-kernel durations with events on the launch stream (a separate pass of K steps)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    app_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    # per-entry-point durations with events on the launch stream (separate passes of K calls)
+    dec_ms = event_times_ms(decode, args.steps, stream)
+    app_ms, _ = graph_call_times_ms([lambda i=i: append(i) for i in range(N_LAYERS)],
+                                    max(1, args.steps // N_LAYERS))
     for d in dev:
         assert torch.isfinite(d["out"].float()).all(), "non-finite decode output"
 
-    dec_b, app_b, kv_b = algorithmic_bytes(wl0)
-    dec_bytes_all = np.mean([algorithmic_bytes(w)[0] for w in layers])
+    _, app_b, _ = algorithmic_bytes(wl0)
+    dec_bytes_all = float(np.mean([algorithmic_bytes(w)[0] for w in layers]))
     value = (dec_bytes_all + app_b) / (ms_per_step * 1e-3) / 1e9
-    dec_avg_s = dec_ms.mean() * 1e-3
-    achieved = dec_bytes_all / dec_avg_s / 1e9
-    traffic = None
-    rec = {
-        "metric": "paged decode KV GB/s (% of HBM peak) + append tokens/s, Llama-8B shape",
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "llama8b-decode-step", "batch": B, "num_q_heads": Hq,
-                   "num_kv_heads": wl0.num_kv_heads, "head_dim": D, "block_size": wl0.block_size,
-                   "context": "U{512..4096} cached + 1 appended", "layers_rotated": N_LAYERS,
-                   "partition_size": args.partition_size or "auto"},
+    config = {"workload": "llama8b-decode-step", "batch": B, "num_q_heads": Hq,
+              "num_kv_heads": wl0.num_kv_heads, "head_dim": D, "block_size": wl0.block_size,
+              "context": "U{512..4096} cached + 1 appended", "layers_rotated": N_LAYERS,
+              "partition_size": args.partition_size or "auto"}
+    rec = base_record(args, METRIC, value, "GB/s", ms_per_step, "bf16", config)
+    ds, aps = stats_us(dec_ms), stats_us(app_ms)
+    rec.update({
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "decode_us_median": round(float(np.median(dec_ms)) * 1e3, 2),
-        "decode_us_p20_p80": [round(float(np.quantile(dec_ms, 0.2)) * 1e3, 2),
-                              round(float(np.quantile(dec_ms, 0.8)) * 1e3, 2)],
-        "append_us_median": round(float(np.median(app_ms)) * 1e3, 2),
-        "append_tokens_per_s": round(B / (float(np.median(app_ms)) * 1e-3), 1),
-        "roofline": {"bound": "hbm", "kernel": "paged_decode (decode_kernel + merge_kernel)",
-                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
-    }
+        "decode_us_median": ds["median"], "decode_us_p20_p80": ds["p20_p80"],
+        "append_us_median": aps["median"],
+        "append_tokens_per_s": round(B / (aps["median"] * 1e-6), 1),
+        "append_timing": "graph replay of the 4 per-layer appends (the kernel alone is launch-bound)",
+        "roofline": hbm_roofline("paged_decode (decode_kernel + merge_kernel)", dec_bytes_all,
+                                 dec_ms.mean() * 1e-3, recorded_traffic()),
+    })
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl0, host_k, host_v)
+    return rec
+
+
+def run_mixed_append(args, P, W):
+    """kv_append of a mixed prefill + decode batch into an fp8 e4m3fn cache; 8 input/pool
+    copies in rotation so that neither the inputs nor the pool stay in the Infinity Cache."""
+    import torch
+    n_copies = 8
+    wl = W.mixed_append("cuda")
+    T = wl.slot_mapping.numel()
+    valid = int((wl.slot_mapping >= 0).sum())
+    H, D, BS, NB = wl.num_kv_heads, wl.head_dim, wl.block_size, wl.num_blocks
+    sets = []
+    for i in range(n_copies):
+        kc = torch.zeros((NB, BS, H, D), dtype=torch.uint8, device="cuda")
+        sets.append(dict(k=wl.new_k.clone(), v=wl.new_v.clone(), slots=wl.slot_mapping.cuda(),
+                         kc=kc, vc=torch.zeros_like(kc),
+                         km=torch.zeros((NB, BS, H), dtype=torch.float32, device="cuda"),
+                         vm=torch.zeros((NB, BS, H), dtype=torch.float32, device="cuda")))
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        s = sets[i % n_copies]
+        P.kv_append(s["k"], s["v"], s["slots"], s["kc"], s["vc"], s["km"], s["vm"],
+                    cache_dtype="fp8")
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(i)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    eager = {k: sets[0][k].clone() for k in ("kc", "vc", "km", "vm")}
+    ms, g = graph_call_times_ms([lambda i=i: call(i) for i in range(n_copies)],
+                                max(1, args.steps // n_copies))
+    for k in eager:                            # one more replay into cleared pools
+        sets[0][k].zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    for k in eager:
+        assert torch.equal(sets[0][k], eager[k]), f"graph replay differs from eager append ({k})"
+    alg = valid * (2 * H * D * 2 + 2 * H * D + 2 * H * 4) + T * 8
+    st = stats_us(ms)
+    config = {"workload": "mixed-prefill-decode-append-fp8", "tokens": T, "valid_tokens": valid,
+              "num_kv_heads": H, "head_dim": D, "block_size": BS, "input": "bf16",
+              "cache": "fp8 e4m3fn + fp32 per-row scale", "copies_rotated": n_copies}
+    rec = base_record(args, "append tokens/s (mixed prefill + decode, fp8 cache)",
+                      valid / (st["mean"] * 1e-6), "tokens/s", ms_per_step, "f32", config)
+    rec.update({"append_us": st, "timing": f"graph replay of the {n_copies} rotated calls",
+                "roofline": hbm_roofline("append_kernel (fp8)", alg, ms.mean() * 1e-3)})
+    return rec
+
+
+def run_long_context(args, P, W):
+    import torch
+    wl = W.long_context("cuda")
+    bt, ctx = wl.block_tables.cuda(), wl.ctx_after.cuda()
+    ps = args.partition_size or 512
+    ws = P.decode_workspace(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                            wl.max_context_len, ps)
+    out = torch.empty_like(wl.q)
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        P.paged_decode(wl.q, wl.k_pool, wl.v_pool, bt, ctx, wl.max_context_len, wl.sm_scale,
+                       partition_size=ps, workspace=ws, out=out)
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(i)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = event_times_ms(call, args.steps, stream)
+    assert torch.isfinite(out.float()).all()
+    alg, kv = decode_bytes(wl, 2 * wl.head_dim * 2)
+    st = stats_us(ms)
+    config = {"workload": "long-context-split-k-decode", "batch": wl.batch,
+              "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
+              "head_dim": wl.head_dim, "block_size": wl.block_size, "context": "U{32768..131072}",
+              "partition_size": ps, "kv_bytes": kv}
+    rec = base_record(args, "paged decode KV GB/s (long context, split-K)",
+                      alg / (st["mean"] * 1e-6) / 1e9, "GB/s", ms_per_step, "bf16", config)
+    rec.update({"decode_us": st, "roofline": hbm_roofline("paged_decode (decode_kernel + merge_kernel)",
+                                                          alg, ms.mean() * 1e-3)})
+    return rec
+
+
+def run_packed3(args, P, W):
+    """3-bit decode; the u3 pools (~232 MB each) are built through the u3 append and four
+    copies are used in rotation so that the Infinity Cache does not hold the one read."""
+    import torch
+    n_copies = 4
+    wl = W.packed3_decode("cuda")
+    NB, BS, H, D = wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim
+    slots = wl.slot_mapping.cuda()
+    pools = []
+    for i in range(n_copies):
+        kc = torch.zeros((NB, BS, H, D * 3 // 32), dtype=torch.int32, device="cuda")
+        vc = torch.zeros_like(kc)
+        km = torch.zeros((NB, BS, H, 2), dtype=torch.float16, device="cuda")
+        vm = torch.zeros_like(km)
+        P.kv_append(wl.new_k, wl.new_v, slots, kc, vc, km, vm, cache_dtype="u3")
+        pools.append((kc, vc, km, vm))
+    torch.cuda.synchronize()
+    n_tok = wl.new_k.shape[0]
+    wl.new_k = wl.new_v = None                 # raw rows no longer needed
+    bt, ctx = wl.block_tables.cuda(), wl.ctx_after.cuda()
+    maxctx = int(wl.ctx_after.max())
+    ps = args.partition_size
+    ws = P.decode_workspace(wl.batch, wl.num_q_heads, H, D, maxctx, ps)
+    out = torch.empty_like(wl.q)
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        kc, vc, km, vm = pools[i % n_copies]
+        P.paged_decode(wl.q, kc, vc, bt, ctx, maxctx, wl.sm_scale, k_meta=km, v_meta=vm,
+                       partition_size=ps, workspace=ws, out=out, cache_dtype="u3")
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(i)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = event_times_ms(call, args.steps, stream)
+    assert torch.isfinite(out.float()).all()
+    alg, kv = decode_bytes(wl, 2 * (D * 3 // 8 + 4))     # 48 B codes + 4 B (s, z), K and V
+    st = stats_us(ms)
+    config = {"workload": "packed3-decode", "batch": wl.batch, "num_q_heads": wl.num_q_heads,
+              "num_kv_heads": H, "head_dim": D, "block_size": BS, "context": "U{1024..16384}",
+              "cache": "3-bit affine, fp16 (scale, zero) per row", "query": "fp16",
+              "tokens": n_tok, "kv_bytes": kv, "copies_rotated": n_copies,
+              "partition_size": ps or "auto"}
+    rec = base_record(args, "paged decode KV GB/s (3-bit packed cache)",
+                      alg / (st["mean"] * 1e-6) / 1e9, "GB/s", ms_per_step, "f16", config)
+    rec.update({"decode_us": st, "roofline": hbm_roofline("paged_decode (decode_kernel u3 + merge_kernel)",
+                                                          alg, ms.mean() * 1e-3)})
+    return rec
+
+
+def run_pack3_exhaustive(args, P, W):
+    """pack3 + unpack3 over every 24-bit octet: values v_j(i) = (i >> 3j) & 7 must pack to
+    the three little-endian bytes of i, and unpack back."""
+    import torch
+    n_oct = 1 << 24
+    i = torch.arange(n_oct, dtype=torch.int32, device="cuda")
+    values = torch.stack([((i >> (3 * j)) & 7).to(torch.uint8) for j in range(8)], dim=1).reshape(-1)
+    want_packed = torch.stack([((i >> (8 * j)) & 255).to(torch.uint8) for j in range(3)], dim=1).reshape(-1)
+    del i
+    packed = torch.empty(3 * n_oct, dtype=torch.uint8, device="cuda")
+    back = torch.empty_like(values)
+    stream = torch.cuda.current_stream()
+    for _ in range(max(1, args.warmup)):
+        P.pack3(values, packed)
+        P.unpack3(packed, values.numel(), back)
+    torch.cuda.synchronize()
+    pk = event_times_ms(lambda _: P.pack3(values, packed), args.steps, stream)
+    up = event_times_ms(lambda _: P.unpack3(packed, values.numel(), back), args.steps, stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    P.pack3(values, packed)
+    P.unpack3(packed, values.numel(), back)
+    ok = bool(torch.equal(packed, want_packed)) and bool(torch.equal(back, values))
+    torch.cuda.synchronize()
+    e2e_ms = (time.perf_counter() - t0) * 1e3
+    assert ok, "exhaustive pack3/unpack3 check failed"
+    ps, us = stats_us(pk), stats_us(up)
+    nbytes = values.numel() + packed.numel()
+    config = {"workload": "pack3-exhaustive-2^24", "octets": n_oct, "values_bytes": values.numel(),
+              "packed_bytes": packed.numel()}
+    rec = base_record(args, "exhaustive 2^24 pack3/unpack3 check time", e2e_ms, "ms", e2e_ms, "u8",
+                      config, higher=False)
+    rec.update({"pack3_us": ps, "unpack3_us": us, "check_passed": ok,
+                "roofline": hbm_roofline("unpack3_kernel", nbytes, us["mean"] * 1e-6)})
+    return rec
+
+
+def run_copy_calibration(args, P, W):
+    """A plain device-to-device copy of 1 GiB (torch's copy kernel): the known-size
+    transfer that the HBM byte counters of the decode kernel are scaled by."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    for _ in range(max(1, args.warmup)):
+        dst.copy_(src)
+    ms = event_times_ms(lambda _: dst.copy_(src), args.steps, stream)
+    st = stats_us(ms)
+    config = {"workload": "copy-calibration", "bytes_read": n, "bytes_written": n}
+    rec = base_record(args, "device copy GB/s (read + write)", 2 * n / (st["mean"] * 1e-6) / 1e9,
+                      "GB/s", st["mean"] * 1e-3, "u8", config)
+    rec["copy_us"] = st
+    return rec
+
+
+WORKLOADS = {"llama8b-decode-step": run_llama8b, "mixed-append-fp8": run_mixed_append,
+             "long-context": run_long_context, "packed3-decode": run_packed3,
+             "pack3-exhaustive": run_pack3_exhaustive, "copy-calibration": run_copy_calibration}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="llama8b-decode-step", choices=sorted(WORKLOADS))
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path has no "
+              "multi-GPU component to measure.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_45_amd as P
+    from paged_kv_cache_45_amd import workloads as W
+
+    torch.cuda.set_device(0)
+    P.load_library()
+    rec = WORKLOADS[args.workload](args, P, W)
     print(json.dumps(rec), flush=True)
 
 
