@@ -86,7 +86,8 @@ typedef enum {
  *                    (s = fp16((max-min)/7), z = fp16(-min/s), q = clamp(rint(x/s+z),
  *                    0, 7); degenerate rows use s = 1, z = fp16(-min)).  Contiguous.
  *                    NULL for same-dtype caches.
- *   head_dim         64 or 128.   block_size 16, 32 or 64.   num_tokens >= 0.
+ *   head_dim         64 or 128.   block_size 16, 32 or 64.   num_tokens >= 0, and
+ *                    num_tokens * num_kv_heads < 2^31 (else PKV_EUNSUPPORTED).
  * Inputs must be finite for the quantised caches.  Bit-exact by contract.
  */
 int kv_append(const void* k_new, const void* v_new, pkv_dtype in_dtype,

@@ -42,13 +42,18 @@ int resolve_partition(int partition_size, int max_context_len, int batch, int nu
 
 constexpr int kMaxPartition = 1 << 20;
 constexpr int kMaxBatch = 8192;       // the decode kernel keeps batch + 1 prefix sums in LDS
+// Share of the units given to the first workgroup on each CU, in 1/16 of the others' share:
+// with two resident workgroups per CU the first one streams ~1.17x faster (measured on the
+// Llama-8B decode step, 86.6 vs 101.6 us mean), and 22/16 evened the tiers out best.
+constexpr int kFirstTierWeight = 22;
 
 struct DecodeLayout {
   pkv::DecodePlan plan;
-  size_t acc_off, ml_off, prefix_off, bytes;
+  size_t acc_off, ml_off, seg_off, bytes;
 };
 
-// Workspace layout of paged_decode: partial accumulators, partial (m, l), prefix sums.
+// Workspace layout of paged_decode: partial accumulators, partial (m, l), and per segment
+// (request, kv-head group) the slot of its first partial and the owner of its last unit.
 DecodeLayout decode_layout(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                            int max_context_len, int ps, int bf16, int kind) {
   DecodeLayout L{};
@@ -58,8 +63,8 @@ DecodeLayout decode_layout(int batch, int num_q_heads, int num_kv_heads, int hea
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   L.acc_off = 0;
   L.ml_off = up(slots * head_dim * sizeof(float));
-  L.prefix_off = L.ml_off + up(slots * 2 * sizeof(float));
-  L.bytes = L.prefix_off + up((size_t)(batch + 1) * sizeof(int));
+  L.seg_off = L.ml_off + up(slots * 2 * sizeof(float));
+  L.bytes = L.seg_off + up((size_t)batch * L.plan.num_head_groups * 2 * sizeof(int));
   return L;
 }
 
@@ -106,6 +111,8 @@ int kv_append(const void* k_new, const void* v_new, pkv_dtype in_dtype,
   // a 16-bit cache must have the input's dtype (no implicit fp16 <-> bf16 conversion)
   if (is16(cache_dtype) && cache_dtype != in_dtype) return PKV_EINVAL;
   if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0) return PKV_EINVAL;
+  // rows (token, kv head) are indexed in 32 bits (2^31 rows of >= 128 bytes exceed any GPU)
+  if (num_tokens >= (int64_t(1) << 31) / num_kv_heads) return PKV_EUNSUPPORTED;
   int st = check_head_dim(head_dim);
   if (st != PKV_OK) return st;
   st = check_block_size(block_size);
@@ -253,6 +260,8 @@ int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
   p.max_context_len = max_context_len;
   p.partition_size = ps;
   p.num_wgs = L.plan.num_wgs;
+  p.split_tier = L.plan.split_tier;
+  p.split_a = kFirstTierWeight;
   p.heads_per_group = L.plan.heads_per_group;
   p.num_head_groups = L.plan.num_head_groups;
   p.token_streams = L.plan.token_streams;
@@ -260,7 +269,7 @@ int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
   char* ws = static_cast<char*>(workspace);
   p.ws_acc = reinterpret_cast<float*>(ws + L.acc_off);
   p.ws_ml = reinterpret_cast<float*>(ws + L.ml_off);
-  p.ws_prefix = reinterpret_cast<int*>(ws + L.prefix_off);
+  p.ws_seg = reinterpret_cast<int*>(ws + L.seg_off);
   const hipError_t e = pkv::launch_decode(p, L.plan, kind, q_dtype == PKV_BF16, head_dim, group, stream);
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
 }

@@ -112,47 +112,78 @@ __device__ __forceinline__ void store_u3_row(const uint4& x, uint32_t* dst_row, 
             ((uint32_t)__builtin_bit_cast(uint16_t, z16) << 16);
 }
 
-template <int D, bool BF16, CacheKind KIND>
+// Each group of D/8 lanes handles R rows (token, kv head), RPB rows apart, so that the
+// block covers R * RPB consecutive rows: all slot ids are loaded first, then the K/V rows of
+// the valid ones, so R rows share one load latency.
+template <int D, bool BF16, CacheKind KIND, int R>
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   constexpr int LPR = D / 8;
   constexpr int RPB = 256 / LPR;
   const int c = threadIdx.x % LPR;
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
-  const int64_t t = row / p.num_kv_heads;
-  const int h = (int)(row - t * p.num_kv_heads);
-  if (t >= p.num_tokens) return;
-  const int64_t slot = p.slots[t];
-  if (slot < 0 || slot >= p.capacity) return;      // padding: no load, no store
-  const int64_t blk = slot >> p.log2_bs;
-  const int64_t off = slot & ((1 << p.log2_bs) - 1);
-  const int64_t crow = blk * p.c_sb + off * p.c_ss + (int64_t)h * p.c_sh;
-  const int64_t mrow = slot * p.num_kv_heads + h;   // meta pools are [NB, BS, Hkv] contiguous
-  const uint4 kx = *reinterpret_cast<const uint4*>(
-      static_cast<const uint16_t*>(p.k_new) + t * p.k_st + h * p.k_sh + c * 8);
-  const uint4 vx = *reinterpret_cast<const uint4*>(
-      static_cast<const uint16_t*>(p.v_new) + t * p.v_st + h * p.v_sh + c * 8);
-  if constexpr (KIND == CacheKind::Same) {
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.k_cache) + crow + c * 8) = kx;
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.v_cache) + crow + c * 8) = vx;
-  } else if constexpr (KIND == CacheKind::Fp8) {
-    store_fp8_row<LPR, BF16>(kx, static_cast<uint8_t*>(p.k_cache) + crow + c * 8,
-                             static_cast<float*>(p.k_meta) + mrow, c);
-    store_fp8_row<LPR, BF16>(vx, static_cast<uint8_t*>(p.v_cache) + crow + c * 8,
-                             static_cast<float*>(p.v_meta) + mrow, c);
-  } else {
-    store_u3_row<LPR, BF16>(kx, static_cast<uint32_t*>(p.k_cache) + crow,
-                            static_cast<uint32_t*>(p.k_meta) + mrow, c);
-    store_u3_row<LPR, BF16>(vx, static_cast<uint32_t*>(p.v_cache) + crow,
-                            static_cast<uint32_t*>(p.v_meta) + mrow, c);
+  const uint32_t row0 = blockIdx.x * (uint32_t)(RPB * R) + threadIdx.x / LPR;
+  const uint32_t H = (uint32_t)p.num_kv_heads;
+  int64_t slot[R];
+  uint32_t tok[R], head[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const uint32_t row = row0 + k * RPB;
+    tok[k] = row / H;
+    head[k] = row - tok[k] * H;
+    slot[k] = tok[k] < (uint64_t)p.num_tokens ? p.slots[tok[k]] : -1;
+  }
+  bool valid[R];
+  uint4 kx[R], vx[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    valid[k] = slot[k] >= 0 && slot[k] < p.capacity;   // padding: no load, no store
+    if (valid[k]) {
+      kx[k] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k_new) +
+                                              (int64_t)tok[k] * p.k_st + (int64_t)head[k] * p.k_sh + c * 8);
+      vx[k] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v_new) +
+                                              (int64_t)tok[k] * p.v_st + (int64_t)head[k] * p.v_sh + c * 8);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    if (!valid[k]) continue;
+    const int64_t blk = slot[k] >> p.log2_bs;
+    const int64_t off = slot[k] & ((1 << p.log2_bs) - 1);
+    const int64_t crow = blk * p.c_sb + off * p.c_ss + (int64_t)head[k] * p.c_sh;
+    const int64_t mrow = slot[k] * p.num_kv_heads + head[k];   // meta pools are [NB, BS, Hkv]
+    if constexpr (KIND == CacheKind::Same) {
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.k_cache) + crow + c * 8) = kx[k];
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.v_cache) + crow + c * 8) = vx[k];
+    } else if constexpr (KIND == CacheKind::Fp8) {
+      store_fp8_row<LPR, BF16>(kx[k], static_cast<uint8_t*>(p.k_cache) + crow + c * 8,
+                               static_cast<float*>(p.k_meta) + mrow, c);
+      store_fp8_row<LPR, BF16>(vx[k], static_cast<uint8_t*>(p.v_cache) + crow + c * 8,
+                               static_cast<float*>(p.v_meta) + mrow, c);
+    } else {
+      store_u3_row<LPR, BF16>(kx[k], static_cast<uint32_t*>(p.k_cache) + crow,
+                              static_cast<uint32_t*>(p.k_meta) + mrow, c);
+      store_u3_row<LPR, BF16>(vx[k], static_cast<uint32_t*>(p.v_cache) + crow,
+                              static_cast<uint32_t*>(p.v_meta) + mrow, c);
+    }
   }
 }
+
+// Rows per lane group: the bit copy takes 4 once the batch fills the chip several times over
+// (more bytes in flight per wave); a small decode append is one latency chain either way and
+// wants as many workgroups as possible.  The quantising kinds are bound by their arithmetic,
+// which 4 rows per lane only serialise (measured slower), so they keep 1.
+constexpr int64_t kAppendManyRows = 256 * 64;
 
 template <int D, bool BF16, CacheKind KIND>
 static hipError_t launch_append_t(const AppendParams& p, hipStream_t s) {
   constexpr int RPB = 256 / (D / 8);
   const int64_t rows = p.num_tokens * p.num_kv_heads;
-  const int64_t blocks = (rows + RPB - 1) / RPB;
-  hipLaunchKernelGGL((append_kernel<D, BF16, KIND>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+  if (KIND == CacheKind::Same && rows >= kAppendManyRows) {
+    const int64_t blocks = (rows + 4 * RPB - 1) / (4 * RPB);
+    hipLaunchKernelGGL((append_kernel<D, BF16, KIND, 4>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+  } else {
+    const int64_t blocks = (rows + RPB - 1) / RPB;
+    hipLaunchKernelGGL((append_kernel<D, BF16, KIND, 1>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 

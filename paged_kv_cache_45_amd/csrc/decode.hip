@@ -48,8 +48,20 @@ __device__ __forceinline__ int clamp_ctx(const DecodeParams& p, int b) {
   return min(max(p.context_lens[b], 0), p.max_context_len);
 }
 
-// Lane geometry for head_dim D with HPI heads per wave instruction.
-template <int D, int HPI>
+// Static split of the units over the grid.  The first workgroup dispatched to each CU is
+// issued ahead of the CU's later ones and streams faster, so the first `split_tier`
+// workgroups carry split_a / 16 of the share of the others: workgroup w starts at unit
+// floor(total * c(w) / c(W)) with c(w) = a * min(w, H) + 16 * max(0, w - H).
+__device__ __forceinline__ int64_t split_c(const DecodeParams& p, int64_t w) {
+  const int64_t h = p.split_tier;
+  return w <= h ? p.split_a * w : p.split_a * h + 16 * (w - h);
+}
+__device__ __forceinline__ int64_t range_start(const DecodeParams& p, int64_t total, int64_t w) {
+  return total * split_c(p, w) / split_c(p, p.num_wgs);
+}
+
+// Lane geometry for head_dim D with HPI heads per wave instruction (G query heads per kv head).
+template <int D, int HPI, int G>
 struct Geo {
   static constexpr int LPR = D / 8;                 // lanes per (head, token) row
   static constexpr int RPI = 64 / LPR;              // rows per wave instruction
@@ -69,24 +81,57 @@ template <int G>
 struct State {
   uint32_t qv[G][4];                 // this lane's 8 query elements of each query head
   float qsum[G];                     // u3: sum of the query row (dequant hoisting)
-  float m[G], l[G], zc[G], acc[G][8];
+  float m[G], l[G], zc[G];
+  // accumulator column e (this lane's d = 8c + e) of query head g is acc4[g / 4][e][g % 4]: the
+  // register quads are the C operands of the PV matrix-core products
+  f32x4_t acc4[(G + 3) / 4][8];
 };
+
+#define PKV_ACC(S, g, e) ((S).acc4[(g) >> 2][e][(g) & 3])
+
+// acc[g][e] += w * p[g] * v[e] for the query heads g of this lane's row.  On the matrix cores:
+// v_mfma_f32_4x4x1f32 runs 16 independent 4x4 outer products per wave, block b taking
+// A[m] from lane 4b + m and B[n] from lane 4b + n and leaving C[m][n] in register m of lane
+// 4b + n.  The 4 lanes of a block lie in one (head, token) row (D/8 lanes, a multiple of 4),
+// all of which hold the row's p[g]; so with A = w * p[lane % 4] and B = v[e] of the lane
+// itself, register m of lane (row, c) gains w * p[m] * v[e], the same as the FMA form.
+// With G = 8 the extra operand registers push the kernel into spills (measured 7 % slower on
+// the long-context decode), so G = 8 keeps the FMA form.
+template <int G, typename St>
+__device__ __forceinline__ void pv_accumulate(St& S, const float (&p)[G], float w, const float (&v)[8]) {
+  if constexpr (G <= 4) {
+    const int q = threadIdx.x & 3;
+    float a = 0.f;                                  // heads g >= G of the quad stay 0
+#pragma unroll
+    for (int m = 0; m < G; ++m) a = (q == m) ? p[m] : a;
+    a *= w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) S.acc4[0][e] = __builtin_amdgcn_mfma_f32_4x4x1f32(a, v[e], S.acc4[0][e], 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float pw = p[g] * w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) PKV_ACC(S, g, e) = fmaf(pw, v[e], PKV_ACC(S, g, e));
+    }
+  }
+}
 
 // Per-lane byte offsets of the rows a lane reads in a chunk (instruction i reads the row
 // TPI*i slots after the lane's first row); the chunk's block and first slot are
 // wave-uniform and kept in scalar registers.
-template <int D, int HPI, CacheKind KIND>
+template <int D, int HPI, CacheKind KIND, int G>
 struct LaneOffsets {
-  static constexpr int NI = Geo<D, HPI>::NI;
+  static constexpr int NI = Geo<D, HPI, G>::NI;
   uint32_t row[NI];                  // bytes from the chunk's uniform row base
   uint32_t meta[NI];                 // u3: bytes from the chunk's uniform meta base
 };
 
-template <int D, int HPI, CacheKind KIND>
-__device__ __forceinline__ LaneOffsets<D, HPI, KIND> lane_offsets(const DecodeParams& p, int tr, int hh,
+template <int D, int HPI, CacheKind KIND, int G>
+__device__ __forceinline__ LaneOffsets<D, HPI, KIND, G> lane_offsets(const DecodeParams& p, int tr, int hh,
                                                                    int c) {
-  using Gm = Geo<D, HPI>;
-  LaneOffsets<D, HPI, KIND> o;
+  using Gm = Geo<D, HPI, G>;
+  LaneOffsets<D, HPI, KIND, G> o;
   constexpr int esz = KIND == CacheKind::U3 ? 4 : 2;
   const int col = KIND == CacheKind::U3 ? ((3 * c) >> 2) : c * 8;
 #pragma unroll
@@ -100,11 +145,11 @@ __device__ __forceinline__ LaneOffsets<D, HPI, KIND> lane_offsets(const DecodePa
 
 // Issue the loads of one chunk: `kb`/`vb` point at the row of (block, first slot, first head
 // of the group) and `kmb`/`vmb` at its meta entry (u3), all wave-uniform.
-template <int D, int HPI, CacheKind KIND>
+template <int D, int HPI, CacheKind KIND, int G>
 __device__ __forceinline__ void load_chunk(const char* kb, const char* vb, const char* kmb,
-                                           const char* vmb, const LaneOffsets<D, HPI, KIND>& o, int c,
-                                           Regs<Geo<D, HPI>::NI, KIND>& R) {
-  using Gm = Geo<D, HPI>;
+                                           const char* vmb, const LaneOffsets<D, HPI, KIND, G>& o, int c,
+                                           Regs<Geo<D, HPI, G>::NI, KIND>& R) {
+  using Gm = Geo<D, HPI, G>;
   if constexpr (KIND == CacheKind::Same) {
 #pragma unroll
     for (int i = 0; i < Gm::NI; ++i) {
@@ -131,9 +176,9 @@ __device__ __forceinline__ void load_chunk(const char* kb, const char* vb, const
 // past t_end are excluded (only the last chunk of a range can be ragged).
 template <int D, int G, bool BF16, CacheKind KIND, int HPI, bool MASKED>
 __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S,
-                                              const Regs<Geo<D, HPI>::NI, KIND>& R, int tok,
+                                              const Regs<Geo<D, HPI, G>::NI, KIND>& R, int tok,
                                               int t_end, int c) {
-  using Gm = Geo<D, HPI>;
+  using Gm = Geo<D, HPI, G>;
   constexpr int NI = Gm::NI, LPR = Gm::LPR;
   bool valid[NI];
 #pragma unroll
@@ -184,20 +229,35 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
       }
     }
   }
+  // Online-softmax update.  The running maxima rarely grow once a few dozen tokens have been
+  // seen, so the rescaling of (l, acc) is skipped for the whole wave when no row's maximum
+  // grew in this chunk: the factor would be exp2(0) = 1 exactly, so the result is the same.
   float pp[NI][G];
+  float mx[G];
+  bool grow = false;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    float mx = sc[0][g];
+    mx[g] = sc[0][g];
 #pragma unroll
-    for (int i = 1; i < NI; ++i) mx = fmaxf(mx, sc[i][g]);
-    const float mn = fmaxf(S.m[g], mx);
-    const float mu = (MASKED && mn == neg_inf()) ? 0.f : mn;   // a row with no token yet
-    const float al = fast_exp2(S.m[g] - mu);
-    S.m[g] = mn;
-    S.l[g] *= al;
-    if constexpr (KIND == CacheKind::U3) S.zc[g] *= al;
+    for (int i = 1; i < NI; ++i) mx[g] = fmaxf(mx[g], sc[i][g]);
+    grow |= mx[g] > S.m[g];
+  }
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) S.acc[g][e] *= al;
+    for (int g = 0; g < G; ++g) {
+      const float mn = fmaxf(S.m[g], mx[g]);
+      const float mu = (MASKED && mn == neg_inf()) ? 0.f : mn;   // a row with no token yet
+      const float al = fast_exp2(S.m[g] - mu);
+      S.m[g] = mn;
+      S.l[g] *= al;
+      if constexpr (KIND == CacheKind::U3) S.zc[g] *= al;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) PKV_ACC(S, g, e) *= al;
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float mu = (MASKED && S.m[g] == neg_inf()) ? 0.f : S.m[g];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       pp[i][g] = fast_exp2(sc[i][g] - mu);
@@ -215,10 +275,7 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
         vf[2 * e] = h_lo<BF16>(vw[e]);
         vf[2 * e + 1] = h_hi<BF16>(vw[e]);
       }
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) S.acc[g][e] = fmaf(pp[i][g], vf[e], S.acc[g][e]);
+      pv_accumulate<G>(S, pp[i], 1.f, vf);
     } else {
       const int sh = (24 * c) & 31;
       const uint32_t vo = __builtin_amdgcn_alignbit(R.vhi[i], R.vlo[i], sh) & 0xffffffu;
@@ -226,14 +283,10 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
       for (int e = 0; e < 8; ++e) vf[e] = (float)((vo >> (3 * e)) & 7u);
       const float vs = valid[i] ? f16_lo(R.vm[i]) : 0.f;
       const float vz = valid[i] ? f16_hi(R.vm[i]) : 0.f;
+      // sum_t p (code - z) s = sum_t (p s) code - sum_t (p s) z
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        // sum_t p (code - z) s = sum_t (p s) code - sum_t (p s) z
-        const float pw = pp[i][g] * vs;
-        S.zc[g] = fmaf(pw, vz, S.zc[g]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) S.acc[g][e] = fmaf(pw, vf[e], S.acc[g][e]);
-      }
+      for (int g = 0; g < G; ++g) S.zc[g] = fmaf(pp[i][g] * vs, vz, S.zc[g]);
+      pv_accumulate<G>(S, pp[i], vs, vf);
     }
   }
 }
@@ -243,14 +296,14 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
 template <int D, int G, bool BF16, CacheKind KIND, int HPI>
 __device__ __forceinline__ void run_range(const DecodeParams& p, State<G>& S, int b, int hg, int t0,
                                           int t1, int lane, int tr, int hh, int c, int stream) {
-  using Gm = Geo<D, HPI>;
+  using Gm = Geo<D, HPI, G>;
   using R = Regs<Gm::NI, KIND>;
   constexpr int esz = KIND == CacheKind::U3 ? 4 : 2;
   const int nk = (t1 - t0 + Gm::CT - 1) / Gm::CT;
   const bool ragged = ((t1 - t0) % Gm::CT) != 0;
   const int32_t* bt_row = p.block_tables + b * p.bt_sb;
   const int h_first = hg * p.heads_per_group;
-  const LaneOffsets<D, HPI, KIND> lo = lane_offsets<D, HPI, KIND>(p, tr, hh, c);
+  const LaneOffsets<D, HPI, KIND, G> lo = lane_offsets<D, HPI, KIND, G>(p, tr, hh, c);
   const char* kc = static_cast<const char*>(p.k_cache) + (int64_t)h_first * p.c_sh * esz;
   const char* vc = static_cast<const char*>(p.v_cache) + (int64_t)h_first * p.c_sh * esz;
   const char* kmc = static_cast<const char*>(p.k_meta) + (int64_t)h_first * 4;
@@ -268,7 +321,7 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, State<G>& S, in
       const int64_t slot0 = tok0 & (p.block_size - 1);
       const int64_t rowb = (phys * p.c_sb + slot0 * p.c_ss) * esz;
       const int64_t metab = ((phys * p.block_size + slot0) * p.num_kv_heads) * 4;
-      load_chunk<D, HPI, KIND>(kc + rowb, vc + rowb, kmc + metab, vmc + metab, lo, c, regs);
+      load_chunk<D, HPI, KIND, G>(kc + rowb, vc + rowb, kmc + metab, vmc + metab, lo, c, regs);
     };
     auto tok_of = [&](int k) { return t0 + (win + k) * Gm::CT + tr; };
     // this stream's chunks k = first, first + ts, ... of the window; the ragged last chunk of
@@ -304,12 +357,12 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, State<G>& S, in
 // Merge the rows of the wave that hold the same head at different token offsets (TPI > 1).
 template <int D, int G, CacheKind KIND, int HPI>
 __device__ __forceinline__ void merge_rows(State<G>& S) {
-  using Gm = Geo<D, HPI>;
+  using Gm = Geo<D, HPI, G>;
   if constexpr (KIND == CacheKind::U3) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) S.acc[g][e] -= S.zc[g];
+      for (int e = 0; e < 8; ++e) PKV_ACC(S, g, e) -= S.zc[g];
   }
 #pragma unroll
   for (int off = HPI * Gm::LPR; off < 64; off <<= 1) {
@@ -323,8 +376,8 @@ __device__ __forceinline__ void merge_rows(State<G>& S) {
       S.l[g] = S.l[g] * fs + lo * fo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float ao = __shfl_xor(S.acc[g][e], off);
-        S.acc[g][e] = S.acc[g][e] * fs + ao * fo;
+        const float ao = __shfl_xor(PKV_ACC(S, g, e), off);
+        PKV_ACC(S, g, e) = PKV_ACC(S, g, e) * fs + ao * fo;
       }
       S.m[g] = mn;
     }
@@ -372,12 +425,10 @@ __device__ __forceinline__ void store_out_row(const DecodeParams& p, int b, int 
 
 template <int D, int G, bool BF16, CacheKind KIND, int HPI>
 __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) {
-  using Gm = Geo<D, HPI>;
+  using Gm = Geo<D, HPI, G>;
   extern __shared__ int s_pref[];              // batch + 1 entries
   __shared__ int s_tile[kMaxWaves];
   build_prefix(p, s_pref, s_tile);
-  if (blockIdx.x == 0)                         // the merge kernel reads the same prefix
-    for (int i = threadIdx.x; i <= p.batch; i += blockDim.x) p.ws_prefix[i] = s_pref[i];
 
   const int lane = threadIdx.x & 63;
   const int hw_count = p.heads_per_group / HPI;  // waves per token stream
@@ -392,10 +443,16 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
   float* s_x = reinterpret_cast<float*>(s_pref + ((p.batch + 1 + 3) & ~3));
   const int64_t NHG = p.num_head_groups;
   const int64_t total = NHG * s_pref[p.batch];            // units of all segments
-  const int64_t nwg = p.num_wgs;
   const int64_t wg = blockIdx.x;
-  int64_t x = wg * total / nwg;
-  const int64_t x_end = (wg + 1) * total / nwg;
+  int64_t x = range_start(p, total, wg);
+  const int64_t x_end = range_start(p, total, wg + 1);
+  if (x == x_end) {            // empty range (fewer units than workgroups): an empty state in slot 0
+    const int n_st = p.heads_per_group * G;
+    for (int i = threadIdx.x; i < n_st * D; i += blockDim.x) p.ws_acc[(wg * 2 * n_st) * D + i] = 0.f;
+    for (int i = threadIdx.x; i < n_st; i += blockDim.x)
+      *reinterpret_cast<float2*>(p.ws_ml + (wg * 2 * n_st + i) * 2) = make_float2(neg_inf(), 0.f);
+    return;
+  }
   bool first = true;
   while (x < x_end) {
     // segment (request b, head group hg) holding unit x: the last b with NHG*s_pref[b] <= x
@@ -411,6 +468,11 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
     const int g0 = (int)(off - (int64_t)hg * n);
     const int g1 = (int)min<int64_t>(n, g0 + (x_end - x));
     const int ctx = clamp_ctx(p, b);
+    if (threadIdx.x == 0) {                    // where the merge kernel finds this segment's pieces
+      const int64_t sidx = (int64_t)b * NHG + hg;
+      if (g0 == 0) p.ws_seg[2 * sidx] = (int)(wg * 2 + (first ? 0 : 1));
+      if (g1 == n) p.ws_seg[2 * sidx + 1] = (int)wg;
+    }
     const int t0 = g0 * p.partition_size;
     const int t1 = min(ctx, g1 * p.partition_size);
     const int hh = wv * HPI + hr;                          // head inside the group
@@ -433,7 +495,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
       S.l[g] = 0.f;
       S.zc[g] = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) S.acc[g][e] = 0.f;
+      for (int e = 0; e < 8; ++e) PKV_ACC(S, g, e) = 0.f;
     }
     run_range<D, G, BF16, KIND, HPI>(p, S, b, hg, t0, t1, lane, tr, hh, c, stream);
     merge_rows<D, G, KIND, HPI>(S);
@@ -443,7 +505,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
         for (int g = 0; g < G; ++g) {
           float* xs = s_x + (((int64_t)(stream - 1) * p.heads_per_group + hh) * G + g) * (D + 2);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) xs[c * 8 + e] = S.acc[g][e];
+          for (int e = 0; e < 8; ++e) xs[c * 8 + e] = PKV_ACC(S, g, e);
           if (c == 0) {
             xs[D] = S.m[g];
             xs[D + 1] = S.l[g];
@@ -462,7 +524,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
             const float fs = fast_exp2(S.m[g] - mu), fo = fast_exp2(mo - mu);
             S.l[g] = S.l[g] * fs + lo2 * fo;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) S.acc[g][e] = S.acc[g][e] * fs + xs[c * 8 + e] * fo;
+            for (int e = 0; e < 8; ++e) PKV_ACC(S, g, e) = PKV_ACC(S, g, e) * fs + xs[c * 8 + e] * fo;
             S.m[g] = mn;
           }
         }
@@ -472,14 +534,19 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
     if (stream == 0 && tr == 0) {
       if (g0 == 0 && g1 == n) {                   // whole segment: final output
 #pragma unroll
-        for (int g = 0; g < G; ++g) store_out_row<BF16>(p, b, h * G + g, c, S.acc[g], 1.f / S.l[g]);
+        for (int g = 0; g < G; ++g) {
+          float a8[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a8[e] = PKV_ACC(S, g, e);
+          store_out_row<BF16>(p, b, h * G + g, c, a8, 1.f / S.l[g]);
+        }
       } else {                                    // part of a split segment
         const int64_t slot = (wg * 2 + (first ? 0 : 1)) * p.heads_per_group + hh;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           float* dst = p.ws_acc + (slot * G + g) * D + c * 8;
-          *reinterpret_cast<float4*>(dst) = make_float4(S.acc[g][0], S.acc[g][1], S.acc[g][2], S.acc[g][3]);
-          *reinterpret_cast<float4*>(dst + 4) = make_float4(S.acc[g][4], S.acc[g][5], S.acc[g][6], S.acc[g][7]);
+          *reinterpret_cast<float4*>(dst) = make_float4(PKV_ACC(S, g, 0), PKV_ACC(S, g, 1), PKV_ACC(S, g, 2), PKV_ACC(S, g, 3));
+          *reinterpret_cast<float4*>(dst + 4) = make_float4(PKV_ACC(S, g, 4), PKV_ACC(S, g, 5), PKV_ACC(S, g, 6), PKV_ACC(S, g, 7));
           if (c == 0) *reinterpret_cast<float2*>(p.ws_ml + (slot * G + g) * 2) = make_float2(S.m[g], S.l[g]);
         }
       }
@@ -505,34 +572,22 @@ __global__ __launch_bounds__(D * kMergeMaxSplit) void merge_kernel(DecodeParams 
   const int b = blockIdx.x / (G * p.num_kv_heads);
   const int hg = kvh / p.heads_per_group, hh = kvh % p.heads_per_group;
   const int d = threadIdx.x % D, part = threadIdx.x / D;
-  const int64_t NHG = p.num_head_groups;
-  const int pb = p.ws_prefix[b], n = p.ws_prefix[b + 1] - pb;
   uint16_t* out = static_cast<uint16_t*>(p.out) + b * p.o_sb + (int64_t)(kvh * G + g) * p.o_sh;
-  if (n == 0) {
+  if (clamp_ctx(p, b) == 0) {
     if (part == 0) out[d] = 0;
     return;
   }
-  const int64_t total = NHG * p.ws_prefix[p.batch];
-  const int64_t nwg = p.num_wgs;
-  const int64_t s0 = NHG * pb + (int64_t)hg * n, s1 = s0 + n - 1;
-  const int64_t w0 = ((s0 + 1) * nwg - 1) / total;     // workgroup that owns unit s0
-  const int64_t w1 = ((s1 + 1) * nwg - 1) / total;
+  // The decode kernel recorded, for this (request, head group) segment, the partial slot of the
+  // workgroup w0 that holds its first unit (2 * w0 + 0 if the segment starts w0's range, else
+  // 2 * w0 + 1) and the workgroup w1 that holds its last unit; w0 + 1 .. w1 keep theirs in
+  // slot 0 (a workgroup with an empty range wrote an empty state there).
+  const int64_t sidx = (int64_t)b * p.num_head_groups + hg;
+  const int64_t first = p.ws_seg[2 * sidx];
+  const int64_t w0 = first >> 1, w1 = p.ws_seg[2 * sidx + 1];
   if (w0 == w1) return;                                // one workgroup covered it and wrote out
-  // Partials: workgroup w0 holds the segment's head in slot 0 if the segment starts its range,
-  // else in slot 1; workgroups w0+1 .. w1 hold the rest in slot 0.  With fewer units than
-  // workgroups some ranges are empty and those workgroups wrote nothing.
-  const bool maybe_empty = total < nwg;
   const int64_t hpg = p.heads_per_group;
   auto slot_of = [&](int64_t j) {        // j-th partial, j = 0 .. w1 - w0
-    const int64_t w = w0 + j;
-    const int s = (j == 0 && w0 * total / nwg != s0) ? 1 : 0;
-    return ((w * 2 + s) * hpg + hh) * G + g;
-  };
-  auto live = [&](int64_t j) {
-    if (j > w1 - w0) return false;
-    if (!maybe_empty || j == 0) return true;
-    const int64_t w = w0 + j;
-    return w * total / nwg < (w + 1) * total / nwg;
+    return ((j == 0 ? first : (w0 + j) * 2) * hpg + hh) * G + g;
   };
   float M = neg_inf(), L = 0.f, A = 0.f;
   for (int64_t j0 = part; j0 <= w1 - w0; j0 += kMergeSplit * kMergeBatch) {
@@ -542,15 +597,15 @@ __global__ __launch_bounds__(D * kMergeMaxSplit) void merge_kernel(DecodeParams 
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {            // independent loads, all in flight
       const int64_t j = j0 + (int64_t)u * kMergeSplit;
-      ok[u] = live(j);
+      ok[u] = j <= w1 - w0;
       const int64_t sl = ok[u] ? slot_of(j) : 0;
       ml[u] = ok[u] ? *reinterpret_cast<const float2*>(p.ws_ml + sl * 2) : make_float2(neg_inf(), 0.f);
       a[u] = ok[u] ? p.ws_acc[sl * D + d] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < kMergeBatch; ++u) {
-      if (!ok[u]) continue;
-      const float mn = fmaxf(M, ml[u].x);              // partial maxima are finite
+      if (!ok[u] || ml[u].x == neg_inf()) continue;    // an empty range's state adds nothing
+      const float mn = fmaxf(M, ml[u].x);
       const float fo = fast_exp2(M - mn), fn = fast_exp2(ml[u].x - mn);
       L = L * fo + ml[u].y * fn;
       A = A * fo + a[u] * fn;
@@ -678,7 +733,9 @@ DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int head_di
     }
   const int64_t units = (int64_t)batch * P.num_head_groups *
                         ((max_context_len + partition_size - 1) / partition_size);
-  P.num_wgs = std::min<int64_t>((int64_t)device_cus() * per_cu, std::max<int64_t>(units, 1));
+  const int cus = device_cus();
+  P.num_wgs = std::min<int64_t>((int64_t)cus * per_cu, std::max<int64_t>(units, 1));
+  P.split_tier = std::min<int64_t>(P.num_wgs, cus);
   return P;
 }
 

@@ -43,13 +43,15 @@ struct DecodeParams {
   int max_context_len;                // context lengths are clamped into [0, max_context_len]
   int partition_size;                 // split granule in tokens, multiple of 16
   int64_t num_wgs;                    // workgroups in the decode grid
+  int64_t split_tier;                 // workgroups of the first dispatch tier (one per CU)
+  int64_t split_a;                    // their share of the units relative to the rest, in 1/16
   int heads_per_group;                // kv heads one workgroup covers
   int num_head_groups;                // num_kv_heads / heads_per_group
   int token_streams;                  // waves sets of a workgroup splitting its chunks
   float scale_log2;                   // sm_scale * log2(e)
   float* ws_acc;                      // [num_wgs, 2, heads_per_group, G, D] partial accumulators
   float* ws_ml;                       // [num_wgs, 2, heads_per_group, G, 2] partial (m, l)
-  int* ws_prefix;                     // [batch + 1] granule prefix sums
+  int* ws_seg;                        // [batch, head groups, 2] first partial slot, last owner
 };
 
 // Launch geometry of paged_decode.
@@ -60,6 +62,7 @@ struct DecodePlan {
   int num_head_groups;
   int token_streams;                  // interleaved chunk streams per workgroup
   int64_t num_wgs;                    // as many as stay resident, at most one per unit
+  int64_t split_tier;                 // first dispatch tier: min(num_wgs, compute units)
   size_t lds_bytes;                   // dynamic LDS of the decode kernel
 };
 

@@ -59,6 +59,7 @@ def _append(lib, **kw):
     (dict(in_dtype=0, cdt=1), -1), (dict(D=96), -2), (dict(D=0), -1), (dict(bs=12), -1),
     (dict(bs=128), -2), (dict(ks_h=4), -1), (dict(k_new=FAKE8), -1), (dict(cdt=2), -1),
     (dict(cdt=3), -1), (dict(nb=0), -1), (dict(H=0), -1), (dict(in_dtype=9), -1),
+    (dict(T=(1 << 31) // 8), -2),
     (dict(ch=-128), -1),
 ])
 def test_append_validation(lib, kw, status):
@@ -98,8 +99,9 @@ def test_workspace_size(lib):
     assert P.paged_decode_workspace_size(0, 32, 8, 128, 512, 0) == 0
     n = P.paged_decode_workspace_size(64, 32, 8, 128, 4097, 0)
     # partials of at most (256 CUs x 8) workgroups x 2 slots x 8 kv heads x G=4 query heads
-    # x (D + 2) floats, plus the prefix sums (each part 256-byte aligned)
-    assert 0 < n <= 2048 * 2 * 8 * 4 * 130 * 4 + 3 * 256 + 65 * 4
+    # x (D + 2) floats, plus two ints per (request, kv-head group) segment (each part 256-byte
+    # aligned)
+    assert 0 < n <= 2048 * 2 * 8 * 4 * 130 * 4 + 3 * 256 + 64 * 8 * 2 * 4
     small = P.paged_decode_workspace_size(2, 4, 4, 64, 26, 0)
     assert 0 < small < n
     for bad in [(64, 32, 8, 128, 4097, 24), (64, 30, 8, 128, 4097, 0), (9000, 32, 8, 128, 10, 0)]:

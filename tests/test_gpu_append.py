@@ -90,14 +90,16 @@ def test_llama8b_decode_append_bf16():
                      wl.num_kv_heads, wl.head_dim)
 
 
+@pytest.mark.parametrize("kind", ["fp8", "same", "u3"])
 @pytest.mark.parametrize("qkv_view", [False, True])
-def test_mixed_append_fp8_full_size(qkv_view):
-    """Mixed prefill + decode append into an fp8 cache with 10% padding (full size)."""
+def test_mixed_append_full_size(kind, qkv_view):
+    """Mixed prefill + decode append with 10% padding at full size (~11.5k tokens x 8 kv
+    heads, enough rows for the multi-row lane groups), into each cache kind."""
     P = need_gpu()
     wl = W.mixed_append("cuda", qkv_view=qkv_view)
     print(f"mixed append: T={wl.slot_mapping.numel()} padding={(wl.slot_mapping < 0).sum().item()} "
-          f"blocks={wl.num_blocks} qkv_view={qkv_view}", flush=True)
-    _run_and_compare(P, "fp8", wl.new_k, wl.new_v, wl.slot_mapping, wl.block_size, wl.num_blocks,
+          f"blocks={wl.num_blocks} qkv_view={qkv_view} kind={kind}", flush=True)
+    _run_and_compare(P, kind, wl.new_k, wl.new_v, wl.slot_mapping, wl.block_size, wl.num_blocks,
                      wl.num_kv_heads, wl.head_dim)
 
 
