@@ -21,6 +21,8 @@ OUT = os.path.join(PKG, "libpagedkv.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["api.cpp", "pack3.hip", "append.hip", "decode.hip"]
 ARCH = "gfx950"
+# test-only kernels (exhaustive checks of internal arithmetic), built beside their tests
+TEST_KERNELS = [os.path.join(ROOT, "tests", "gpu_kernels", "fp8_checks.hip")]
 
 
 def hipcc() -> str:
@@ -62,7 +64,25 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"linking failed:\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, OUT)
+    for src in TEST_KERNELS:
+        _build_test_kernel(src, verbose)
     return OUT
+
+
+def test_kernel_path(src: str) -> str:
+    return os.path.join(os.path.dirname(src), "libpkv_" + os.path.splitext(os.path.basename(src))[0] + ".so")
+
+
+def _build_test_kernel(src: str, verbose: bool) -> str:
+    out = test_kernel_path(src)
+    cmd = [hipcc()] + common_flags() + ["-shared", "-x", "hip", src, "-o", out + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"compiling {src} failed:\n{res.stdout}\n{res.stderr}")
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":

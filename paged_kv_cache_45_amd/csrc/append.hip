@@ -4,8 +4,9 @@
 // slot < 0 marks padding and nothing of that token is loaded; block = slot / block_size,
 // offset = slot % block_size (shift and mask, block_size a power of two); K and V are
 // written by the same thread group; quantised caches divide by the scale in fp32 and
-// only then convert.  The 3-bit cache follows "triton-3bit-kv-cache-kernel" README,
-// sections 1A/1B (bit layout) and section 2 test 3 (fp16 affine scale and zero).
+// only then convert (fp8 arithmetic in fp8_quant.cuh).  The 3-bit cache follows
+// "triton-3bit-kv-cache-kernel" README, sections 1A/1B (bit layout) and section 2 test 3
+// (fp16 affine scale and zero).
 //
 // Work mapping (wave64): one (token, kv head) row per group of D/8 lanes, each lane
 // owning 8 consecutive elements (one 16-byte load of K and one of V).  A 256-thread
@@ -13,29 +14,9 @@
 // row with DPP inside the lane group, so no barrier and no LDS are involved.
 #include "launch.h"
 #include "common.cuh"
+#include "fp8_quant.cuh"
 
 namespace pkv {
-
-// OCP E4M3 (finite-only, bias 7, max 448) code of a finite fp32 value with |y| <= 448,
-// rounded to nearest even; the sign of zero is kept.
-__device__ __forceinline__ uint32_t e4m3fn_code(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  uint32_t code;
-  if (a >= 0x3C800000u) {
-    // |y| >= 2^-6, a normal e4m3 binade: keep 3 of the 23 fp32 mantissa bits, rounding the
-    // 20 dropped bits to nearest even (a carry may step into the next binade), then move
-    // the exponent bias from 127 to 7.
-    const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
-    code = r - (120u << 3);
-  } else {
-    // |y| < 2^-6: multiples of 2^-9 (subnormals, and 8 * 2^-9 = 2^-6 on round-up).
-    // The scaling by 2^9 is exact.
-    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
-  }
-  return code | sign;
-}
 
 template <bool BF16>
 __device__ __forceinline__ void widen8(const uint4& x, float (&f)[8]) {
@@ -47,7 +28,7 @@ __device__ __forceinline__ void widen8(const uint4& x, float (&f)[8]) {
   }
 }
 
-// fp8 row: s = absmax / 448 (1 for an all-zero row), code = RNE(clamp(x / s, +-448)).
+// fp8 row: s = absmax / 448 (1 for an all-zero row), code = RNE_e4m3fn(clamp(x / s, +-448)).
 template <int LPR, bool BF16>
 __device__ __forceinline__ void store_fp8_row(const uint4& x, uint8_t* dst, float* meta, int c) {
   float f[8];
@@ -55,19 +36,19 @@ __device__ __forceinline__ void store_fp8_row(const uint4& x, uint8_t* dst, floa
   float a = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(f[e]));
-  a = group_max<LPR>(a);
-  const float s = (a == 0.f) ? 1.f : a / 448.f;
-  uint32_t lo = 0, hi = 0;
+  const Fp8RowScale q = fp8_row_scale(group_max<LPR>(a));
+  // fp8_scaled per value, with the rare full-division rows handled in one wave-uniform branch
+  float y[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float y = f[e] / s;
-    y = fminf(fmaxf(y, -448.f), 448.f);
-    const uint32_t code = e4m3fn_code(y);
-    if (e < 4) lo |= code << (8 * e);
-    else hi |= code << (8 * (e - 4));
+  for (int e = 0; e < 8; ++e) y[e] = fp8_scaled_fast(f[e], q);
+  if (__builtin_amdgcn_ballot_w64(!q.fast) != 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (!q.fast) y[e] = fp8_scaled_div(f[e], q);
   }
-  *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
-  if (c == 0) *meta = s;
+  *reinterpret_cast<uint2*>(dst) = make_uint2(fp8_pack4(y[0], y[1], y[2], y[3]),
+                                              fp8_pack4(y[4], y[5], y[6], y[7]));
+  if (c == 0) *meta = q.s;
 }
 
 // u3 row: min/max affine parameters in fp32 rounded to fp16, codes clamp(rint(x/s + z), 0, 7),

@@ -1,0 +1,60 @@
+// fp8 e4m3fn quantisation arithmetic of one cache row.
+//
+// "Write Triton Kv Cache Append Kernel", Required reasoning process step 6 and Failure modes:
+// each value is divided by the row's scale in fp32 before it is cast, and the cast saturates
+// (here: clamp to +-448 first).  The format is OCP E4M3 finite-only (bias 7, max 448), rounded
+// to nearest even.
+//
+// Two shortcuts keep this cheap on gfx950, both checked exhaustively against the plain
+// definitions (tests/gpu_kernels/fp8_checks.hip, run by tests/test_gpu_fp8_exhaustive.py):
+//  * the quotient x / s of a whole row comes from one correctly rounded reciprocal r = 1 / s
+//    and one fma correction per value, q = fma(fma(-s, x r, x), r, x r) with the sign of x.
+//    q can differ from the correctly rounded x / s in its last bit, but for every 16-bit (fp16
+//    or bf16) x with |x| <= absmax and every 16-bit absmax, its e4m3 code is the code of the
+//    correctly rounded quotient.  Scales outside [2^-100, 2^100] (reciprocal overflow,
+//    subnormal products) take the full division.
+//  * the cast is v_cvt_pk_fp8_f32 (two values per instruction, OCP E4M3 on gfx950, RNE under
+//    the default rounding mode), which equals the integer round-to-nearest-even encoder for
+//    every fp32 value in [-448, 448], and torch's CPU float8_e4m3fn cast.
+#pragma once
+#include <stdint.h>
+
+namespace pkv {
+
+struct Fp8RowScale {
+  float s;      // the stored scale: absmax / 448, or 1 for an all-zero row
+  float r;      // 1 / s, correctly rounded
+  bool fast;    // the one-reciprocal quotient applies
+};
+
+__device__ __forceinline__ Fp8RowScale fp8_row_scale(float absmax) {
+  Fp8RowScale q;
+  q.s = (absmax == 0.f) ? 1.f : absmax / 448.f;
+  q.r = 1.f / q.s;
+  q.fast = q.s >= 0x1p-100f && q.s <= 0x1p100f;
+  return q;
+}
+
+// clamp(x / s, -448, 448) through the reciprocal (valid when q.fast) ...
+__device__ __forceinline__ float fp8_scaled_fast(float x, const Fp8RowScale& q) {
+  const float y0 = x * q.r;
+  const float y = __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q.s, y0, x), q.r, y0), x);
+  return fminf(fmaxf(y, -448.f), 448.f);
+}
+// ... and through a full division (always valid)
+__device__ __forceinline__ float fp8_scaled_div(float x, const Fp8RowScale& q) {
+  return fminf(fmaxf(x / q.s, -448.f), 448.f);
+}
+// the value the append kernel stores the code of
+__device__ __forceinline__ float fp8_scaled(float x, const Fp8RowScale& q) {
+  return q.fast ? fp8_scaled_fast(x, q) : fp8_scaled_div(x, q);
+}
+
+// e4m3fn codes of four clamped values, byte j = code of y_j.
+__device__ __forceinline__ uint32_t fp8_pack4(float y0, float y1, float y2, float y3) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, w, true);
+  return (uint32_t)w;
+}
+
+}  // namespace pkv

@@ -1,0 +1,67 @@
+"""Exhaustive checks of the two shortcuts in the fp8 append arithmetic (fp8_quant.cuh).
+
+1. The row quotient from one reciprocal and one fma correction yields the same e4m3fn code as
+   the correctly rounded x / s, for every 16-bit (fp16 and bf16) x with |x| <= absmax and every
+   finite 16-bit absmax: this is the whole input domain of the quantiser.
+2. The hardware cast v_cvt_pk_fp8_f32 equals the plain integer round-to-nearest-even encoder
+   for every fp32 value in [-448, 448], and torch's CPU float8_e4m3fn cast (which the oracle
+   is pinned to) for every fp32 value in [0, 448].
+
+The kernels live in tests/gpu_kernels/fp8_checks.hip and include the library's header, so
+the checked code is the code the append kernel runs.
+"""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import need_gpu
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB = os.path.join(HERE, "gpu_kernels", "libpkv_fp8_checks.so")
+MAX_BITS = 0x43E00000       # fp32 bit pattern of 448
+
+
+def _lib():
+    need_gpu()
+    if not os.path.exists(LIB):
+        raise RuntimeError(f"{LIB} is not built; run paged_kv_cache_45_amd.build.build() first")
+    lib = ctypes.CDLL(LIB)
+    vp = ctypes.c_void_p
+    lib.fp8chk_hw_codes.argtypes = [ctypes.c_uint32, ctypes.c_uint32, vp, vp, vp]
+    lib.fp8chk_quotient_codes.argtypes = [ctypes.c_int, vp, vp]
+    return lib
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("bf16", [1, 0])
+def test_row_quotient_codes_match_correct_division(bf16):
+    lib = _lib()
+    bad = torch.zeros(32768 * 256, dtype=torch.int32, device="cuda")
+    assert lib.fp8chk_quotient_codes(bf16, bad.data_ptr(), torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    assert int(bad.long().sum()) == 0
+
+
+@pytest.mark.gpu
+def test_hardware_cast_matches_rne_and_torch_cpu_cast():
+    lib = _lib()
+    chunk = 1 << 27
+    codes = torch.empty(chunk, dtype=torch.uint8, device="cuda")
+    bad = torch.empty(chunk // 256, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    total_bad = 0
+    for u0 in range(0, MAX_BITS + 1, chunk):
+        n = min(chunk, MAX_BITS + 1 - u0)
+        nt = (n + 255) // 256
+        bad.zero_()
+        assert lib.fp8chk_hw_codes(u0, nt, codes.data_ptr(), bad.data_ptr(), stream) == 0
+        torch.cuda.synchronize()
+        total_bad += int(bad.long().sum())
+        vals = torch.from_numpy(np.arange(u0, u0 + n, dtype=np.uint32).view(np.float32))
+        want = vals.to(torch.float8_e4m3fn).view(torch.uint8)
+        got = codes[:n].cpu()
+        assert torch.equal(got, want), f"hardware cast differs from torch's CPU cast in [{u0:#x}, {u0 + n:#x})"
+    assert total_bad == 0, "hardware cast differs from the integer RNE encoder"
