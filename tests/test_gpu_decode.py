@@ -223,3 +223,25 @@ def test_rejects_bad_arguments():
     with pytest.raises(P.PagedKVError):      # workspace too small
         P.paged_decode(wl.q, wl.k_pool, wl.v_pool, wl.block_tables.cuda(), wl.ctx_after.cuda(), 26,
                        partition_size=16, workspace=torch.zeros(16, dtype=torch.uint8, device="cuda"))
+
+
+def test_workspace_reused_across_calls():
+    """One workspace serves consecutive calls of different batch sizes and partition sizes: each
+    call overwrites every partial state and segment record it reads, whatever an earlier call of
+    another shape left there."""
+    P = need_gpu()
+    big = W.llama8b_decode("cuda", batch=48, seed=W.BASE_SEED + 21)
+    small = W.llama8b_decode("cuda", batch=5, seed=W.BASE_SEED + 22)
+    ws = P.decode_workspace(big.batch, big.num_q_heads, big.num_kv_heads, big.head_dim,
+                            int(big.ctx_before.max()), 16)
+    ws.fill_(0x5A)                    # stale bytes: nothing may depend on a clean workspace
+    for rep, (wl, ps) in enumerate([(big, 0), (small, 0), (big, 16), (small, 64), (big, 0)]):
+        need = P.paged_decode_workspace_size(wl.batch, wl.num_q_heads, wl.num_kv_heads,
+                                             wl.head_dim, int(wl.ctx_before.max()), ps)
+        assert need <= ws.numel()
+        out = _decode(P, wl, wl.k_pool, wl.v_pool, wl.ctx_before, partition_size=ps, workspace=ws)
+        heads = [(b, h) for b in range(min(wl.batch, 6)) for h in range(wl.num_q_heads)]
+        want = _oracle_same(wl, wl.k_pool, wl.v_pool, wl.ctx_before, heads=heads)
+        sel = np.array([b for b, _ in heads]), np.array([h for _, h in heads])
+        assert report(f"reuse {rep} B={wl.batch} ps={ps}", f32_of(out)[sel], want[sel],
+                      wl.dtype) <= ATTN_TOL
