@@ -106,11 +106,13 @@ int kv_append(const void* k_new, const void* v_new, pkv_dtype in_dtype,
  * Split-K ("flash-decoding", named by [3bit] in its title paragraph as the form of its fused
  * decode): the context of each (request, kv head) may be cut into token ranges that are
  * reduced independently and merged by log-sum-exp.  The library balances the work by
- * giving each resident wave of the current device an equal share of all
+ * giving each resident workgroup of the current device an equal share of all
  * (request, kv head, granule) units, where a granule is `partition_size` tokens; a context
- * is only ever cut at a multiple of the granule.  The workspace holds the partial states
- * of the ranges that get cut, so its size depends on the current device's compute-unit
- * count: query it on the device that will run the call.
+ * is cut at multiples of the granule, except that where a block of the cache holds at least
+ * 64 KB of a wave's K/V the workgroups sharing a context hand its blocks out among
+ * themselves at run time.  The workspace holds the partial states of the ranges that get
+ * cut, so its size depends on the current device's compute-unit count: query it on the
+ * device that will run the call.
  * partition_size: 0 = automatic (16 tokens, the finest balance), else a multiple of 16.
  * Returns 0 for batch 0 and (size_t)-1 for invalid arguments (batch above 8192 included).
  */
@@ -142,8 +144,13 @@ size_t paged_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads,
  *   partition_size   split granule in tokens (0 = automatic; else a multiple of 16); see
  *                    paged_decode_workspace_size.
  *   workspace        device, >= paged_decode_workspace_size(...) bytes, 256-byte aligned,
- *                    no initialisation needed (every call overwrites what it reads).
- *                    One workspace per stream: calls sharing it must be ordered.
+ *                    zero-filled once before its first use.  Its first 256 KB hold counters
+ *                    through which the workgroups sharing a (request, head group) hand out its
+ *                    blocks at run time; every call leaves them at zero again and overwrites
+ *                    all else it reads, so one workspace serves calls of every shape it is
+ *                    large enough for.  (Contents that are not zero there make a call lose
+ *                    work, not fault.)  One workspace per stream: calls sharing it must be
+ *                    ordered.
  *   batch            0 .. 8192.
  * Accumulation is fp32; outputs are rounded to q_dtype to nearest even.
  */

@@ -46,10 +46,13 @@ constexpr int kMaxBatch = 8192;       // the decode kernel keeps batch + 1 prefi
 // with two resident workgroups per CU the first one streams ~1.17x faster (measured on the
 // Llama-8B decode step, 86.6 vs 101.6 us mean), and 22/16 evened the tiers out best.
 constexpr int kFirstTierWeight = 22;
+// Block counters kept at the head of every decode workspace (4 per (request, kv-head group)
+// segment); calls with more segments use the static split only.
+constexpr size_t kClaimSlots = 65536;
 
 struct DecodeLayout {
   pkv::DecodePlan plan;
-  size_t acc_off, ml_off, seg_off, bytes;
+  size_t claim_off, acc_off, ml_off, seg_off, bytes;
 };
 
 // Workspace layout of paged_decode: partial accumulators, partial (m, l), and per segment
@@ -61,8 +64,12 @@ DecodeLayout decode_layout(int batch, int num_q_heads, int num_kv_heads, int hea
   L.plan = pkv::plan_decode(batch, num_q_heads, num_kv_heads, head_dim, max_context_len, ps, bf16, kind);
   const size_t slots = (size_t)L.plan.num_wgs * 2 * L.plan.heads_per_group * group;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  L.acc_off = 0;
-  L.ml_off = up(slots * head_dim * sizeof(float));
+  // The block counters come first, at a fixed size: they must be zero when a call starts, and a
+  // region whose place does not depend on the call's shape keeps them apart from the partials
+  // that an earlier call of another shape wrote into the same workspace.
+  L.claim_off = 0;
+  L.acc_off = kClaimSlots * sizeof(int);
+  L.ml_off = L.acc_off + up(slots * head_dim * sizeof(float));
   L.seg_off = L.ml_off + up(slots * 2 * sizeof(float));
   L.bytes = L.seg_off + up((size_t)batch * L.plan.num_head_groups * 2 * sizeof(int));
   return L;
@@ -270,6 +277,18 @@ int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
   p.ws_acc = reinterpret_cast<float*>(ws + L.acc_off);
   p.ws_ml = reinterpret_cast<float*>(ws + L.ml_off);
   p.ws_seg = reinterpret_cast<int*>(ws + L.seg_off);
+  p.ws_claim = reinterpret_cast<int*>(ws + L.claim_off);
+  // Block claiming: a wave can only take whole blocks, and its share of the bandwidth is small
+  // (~1/2000 of the device), so a claim of B bytes keeps it busy for ~B / 3 GB/s.  It pays only
+  // where blocks are large enough for the claims to outweigh their cost and coarse enough split
+  // granules leave a tail (measured: 128 KB blocks of the long-context decode gain ~10 %, 32 KB
+  // blocks of the Llama-8B step lose 15 %): at least 64 KB of K/V per wave and block.  It also
+  // needs an even number of chunks per block and at most 4 head waves.
+  const int64_t row_bytes = cache_dtype == PKV_U3 ? 2 * (head_dim * 3 / 8 + 4) : 4 * (int64_t)head_dim;
+  const int64_t wave_block_bytes = (int64_t)block_size * L.plan.hpi * row_bytes;
+  p.claim_blocks = (wave_block_bytes >= 64 * 1024 && block_size % (L.plan.chunk_tokens * 2) == 0 &&
+                    L.plan.heads_per_group / L.plan.hpi <= 4 &&
+                    (size_t)batch * L.plan.num_head_groups * 4 <= kClaimSlots) ? 1 : 0;
   const hipError_t e = pkv::launch_decode(p, L.plan, kind, q_dtype == PKV_BF16, head_dim, group, stream);
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
 }

@@ -41,6 +41,7 @@
 namespace pkv {
 
 constexpr int kMaxWaves = 8;        // waves per workgroup at most (token streams x head group)
+constexpr int kClaimWaves = 4;      // block counters per segment (one per head wave)
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 
@@ -354,6 +355,68 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, State<G>& S, in
   }
 }
 
+// The full blocks [0, nbf) of a segment shared by several workgroups, handed out one block at
+// a time to each wave from a counter of the segment in the workspace (one counter per head
+// wave, shared by that head wave's token streams in every sharing workgroup): whichever wave is
+// ready takes the next block, so the sharers, which run on different XCDs at different speeds,
+// finish the segment together instead of each finishing a fixed share.  Per wave, with no
+// barrier: lane 0 claims one block ahead of the one being read, the block id comes through the
+// scalar cache (so its wait never drains the vector loads), and the next block's first chunk is
+// issued before the current block's last chunk is computed.  A wave reads all `my_n` chunks of
+// each block it claims (an even count).
+template <int D, int G, bool BF16, CacheKind KIND, int HPI>
+__device__ __forceinline__ void run_claimed(const DecodeParams& p, State<G>& S, int b, int hg, int nbf,
+                                            int* claim, int lane, int tr, int hh, int c, int stream) {
+  using Gm = Geo<D, HPI, G>;
+  using R = Regs<Gm::NI, KIND>;
+  constexpr int esz = KIND == CacheKind::U3 ? 4 : 2;
+  const int my_n = p.block_size / Gm::CT;                 // chunks per block
+  typedef const __attribute__((address_space(4))) int32_t* ConstIntPtr;
+  const ConstIntPtr bt_row = (ConstIntPtr)(p.block_tables + b * p.bt_sb);
+  const int h_first = hg * p.heads_per_group;
+  const LaneOffsets<D, HPI, KIND, G> lo = lane_offsets<D, HPI, KIND, G>(p, tr, hh, c);
+  const char* kc = static_cast<const char*>(p.k_cache) + (int64_t)h_first * p.c_sh * esz;
+  const char* vc = static_cast<const char*>(p.v_cache) + (int64_t)h_first * p.c_sh * esz;
+  const char* kmc = static_cast<const char*>(p.k_meta) + (int64_t)h_first * 4;
+  const char* vmc = static_cast<const char*>(p.v_meta) + (int64_t)h_first * 4;
+  // a claim outside [0, nbf) ends the loop: a counter that is not zero at the start of the call
+  // (a workspace that was not zero-filled) can only lose work, never read outside the segment
+  auto take = [&](int v) { return (unsigned)v < (unsigned)nbf ? v : nbf; };
+  auto claim_async = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(claim, 1);
+    return v;
+  };
+  auto phys_of = [&](int u) {
+    return u < nbf ? (int64_t)min<int64_t>(max(bt_row[u], 0), p.num_blocks - 1) : (int64_t)0;
+  };
+  auto issue = [&](int64_t phys, int k, R& regs) {          // chunk k (in tokens k * CT) of a block
+    const int64_t slot0 = k * Gm::CT;
+    const int64_t rowb = (phys * p.c_sb + slot0 * p.c_ss) * esz;
+    const int64_t metab = ((phys * p.block_size + slot0) * p.num_kv_heads) * 4;
+    load_chunk<D, HPI, KIND, G>(kc + rowb, vc + rowb, kmc + metab, vmc + metab, lo, c, regs);
+  };
+  int uc = take(__builtin_amdgcn_readfirstlane(claim_async()));
+  int un = take(__builtin_amdgcn_readfirstlane(claim_async()));
+  int64_t pc = phys_of(uc);
+  R ra, rb;
+  if (uc < nbf) issue(pc, 0, ra);
+  while (uc < nbf) {
+    const int pending = (un < nbf) ? claim_async() : 0;   // the claim after next
+    const int64_t pn = phys_of(un);
+    for (int k = 0; k < my_n; k += 2) {
+      issue(pc, k + 1, rb);
+      compute_chunk<D, G, BF16, KIND, HPI, false>(p, S, ra, uc * p.block_size + k * Gm::CT + tr, 0, c);
+      if (k + 2 < my_n) issue(pc, k + 2, ra);
+      else if (un < nbf) issue(pn, 0, ra);
+      compute_chunk<D, G, BF16, KIND, HPI, false>(p, S, rb, uc * p.block_size + (k + 1) * Gm::CT + tr, 0, c);
+    }
+    uc = un;
+    pc = pn;
+    un = (un < nbf) ? take(__builtin_amdgcn_readfirstlane(pending)) : nbf;
+  }
+}
+
 // Merge the rows of the wave that hold the same head at different token offsets (TPI > 1).
 template <int D, int G, CacheKind KIND, int HPI>
 __device__ __forceinline__ void merge_rows(State<G>& S) {
@@ -497,7 +560,18 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
 #pragma unroll
       for (int e = 0; e < 8; ++e) PKV_ACC(S, g, e) = 0.f;
     }
-    run_range<D, G, BF16, KIND, HPI>(p, S, b, hg, t0, t1, lane, tr, hh, c, stream);
+    if (p.claim_blocks && !(g0 == 0 && g1 == n)) {
+      // a shared segment: its full blocks by claim; the ragged tail (if any) by the workgroup
+      // that holds the segment's last unit
+      const int nbf = ctx >> p.log2_bs;
+      run_claimed<D, G, BF16, KIND, HPI>(p, S, b, hg, nbf,
+                                         p.ws_claim + ((int64_t)b * NHG + hg) * kClaimWaves + wv,
+                                         lane, tr, hh, c, stream);
+      if (g1 == n && (nbf << p.log2_bs) < ctx)
+        run_range<D, G, BF16, KIND, HPI>(p, S, b, hg, nbf << p.log2_bs, ctx, lane, tr, hh, c, stream);
+    } else {
+      run_range<D, G, BF16, KIND, HPI>(p, S, b, hg, t0, t1, lane, tr, hh, c, stream);
+    }
     merge_rows<D, G, KIND, HPI>(S);
     if (p.token_streams > 1) {
       if (stream > 0 && tr == 0) {
@@ -573,6 +647,9 @@ __global__ __launch_bounds__(D * kMergeMaxSplit) void merge_kernel(DecodeParams 
   const int hg = kvh / p.heads_per_group, hh = kvh % p.heads_per_group;
   const int d = threadIdx.x % D, part = threadIdx.x / D;
   uint16_t* out = static_cast<uint16_t*>(p.out) + b * p.o_sb + (int64_t)(kvh * G + g) * p.o_sh;
+  // the decode kernel has finished: leave the segment's block counters at zero for the next call
+  if (p.claim_blocks && hh == 0 && g == 0 && threadIdx.x < kClaimWaves)
+    p.ws_claim[((int64_t)b * p.num_head_groups + hg) * kClaimWaves + threadIdx.x] = 0;
   if (clamp_ctx(p, b) == 0) {
     if (part == 0) out[d] = 0;
     return;
@@ -719,6 +796,10 @@ DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int head_di
   P.token_streams = (2 * hw <= kMaxWaves) ? 2 : 1;
   P.waves_per_wg = hw * P.token_streams;
   P.heads_per_group = P.hpi * hw;
+  {
+    const int rpi = 64 / (head_dim / 8), tpi = rpi / P.hpi, ni = std::min(4, 16 / tpi);
+    P.chunk_tokens = ni * tpi;
+  }
   P.num_head_groups = num_kv_heads / P.heads_per_group;
   const int group = num_q_heads / num_kv_heads;
   P.lds_bytes = (size_t)((batch + 1 + 3) & ~3) * sizeof(int) +

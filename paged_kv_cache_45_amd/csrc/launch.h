@@ -52,6 +52,8 @@ struct DecodeParams {
   float* ws_acc;                      // [num_wgs, 2, heads_per_group, G, D] partial accumulators
   float* ws_ml;                       // [num_wgs, 2, heads_per_group, G, 2] partial (m, l)
   int* ws_seg;                        // [batch, head groups, 2] first partial slot, last owner
+  int* ws_claim;                      // [batch, head groups, 4] block counters (zero between calls)
+  int claim_blocks;                   // shared segments hand out their blocks dynamically
 };
 
 // Launch geometry of paged_decode.
@@ -63,6 +65,7 @@ struct DecodePlan {
   int token_streams;                  // interleaved chunk streams per workgroup
   int64_t num_wgs;                    // as many as stay resident, at most one per unit
   int64_t split_tier;                 // first dispatch tier: min(num_wgs, compute units)
+  int chunk_tokens;                   // tokens per chunk of a token stream
   size_t lds_bytes;                   // dynamic LDS of the decode kernel
 };
 

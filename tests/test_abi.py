@@ -99,9 +99,9 @@ def test_workspace_size(lib):
     assert P.paged_decode_workspace_size(0, 32, 8, 128, 512, 0) == 0
     n = P.paged_decode_workspace_size(64, 32, 8, 128, 4097, 0)
     # partials of at most (256 CUs x 8) workgroups x 2 slots x 8 kv heads x G=4 query heads
-    # x (D + 2) floats, plus two ints per (request, kv-head group) segment (each part 256-byte
-    # aligned)
-    assert 0 < n <= 2048 * 2 * 8 * 4 * 130 * 4 + 3 * 256 + 64 * 8 * 2 * 4
+    # x (D + 2) floats, two ints per (request, kv-head group) segment (each part 256-byte
+    # aligned), and the fixed region of 65536 block counters
+    assert 0 < n <= 2048 * 2 * 8 * 4 * 130 * 4 + 3 * 256 + 64 * 8 * 2 * 4 + 65536 * 4
     small = P.paged_decode_workspace_size(2, 4, 4, 64, 26, 0)
     assert 0 < small < n
     for bad in [(64, 32, 8, 128, 4097, 24), (64, 30, 8, 128, 4097, 0), (9000, 32, 8, 128, 10, 0)]:

@@ -226,15 +226,14 @@ def test_rejects_bad_arguments():
 
 
 def test_workspace_reused_across_calls():
-    """One workspace serves consecutive calls of different batch sizes and partition sizes: each
-    call overwrites every partial state and segment record it reads, whatever an earlier call of
-    another shape left there."""
+    """One zero-filled workspace serves consecutive calls of different batch sizes and partition
+    sizes: the block counters that the sharing workgroups claim from are left at zero by every
+    call, and each call overwrites every partial state and segment record it reads."""
     P = need_gpu()
     big = W.llama8b_decode("cuda", batch=48, seed=W.BASE_SEED + 21)
     small = W.llama8b_decode("cuda", batch=5, seed=W.BASE_SEED + 22)
     ws = P.decode_workspace(big.batch, big.num_q_heads, big.num_kv_heads, big.head_dim,
                             int(big.ctx_before.max()), 16)
-    ws.fill_(0x5A)                    # stale bytes: nothing may depend on a clean workspace
     for rep, (wl, ps) in enumerate([(big, 0), (small, 0), (big, 16), (small, 64), (big, 0)]):
         need = P.paged_decode_workspace_size(wl.batch, wl.num_q_heads, wl.num_kv_heads,
                                              wl.head_dim, int(wl.ctx_before.max()), ps)
@@ -245,3 +244,18 @@ def test_workspace_reused_across_calls():
         sel = np.array([b for b, _ in heads]), np.array([h for _, h in heads])
         assert report(f"reuse {rep} B={wl.batch} ps={ps}", f32_of(out)[sel], want[sel],
                       wl.dtype) <= ATTN_TOL
+
+
+def test_block_claiming_ragged():
+    """Contexts shared by several workgroups whose 64-token blocks (128 KB of a wave's K/V) are
+    handed out at run time: ragged lengths, one-block and one-token contexts, all heads."""
+    P = need_gpu()
+    lens = [1, 63, 64, 65, 5000, 20011, 129, 12345]
+    wl = W.decode_workload("claims", batch=len(lens), num_q_heads=32, num_kv_heads=8, head_dim=128,
+                           block_size=64, ctx_lo=0, ctx_hi=0, dtype=torch.bfloat16, device="cuda",
+                           seed=W.BASE_SEED + 31, append_one=False, ctx_override=lens)
+    ws = P.decode_workspace(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, max(lens), 0)
+    want = _oracle_same(wl, wl.k_pool, wl.v_pool, wl.ctx_after)
+    for rep in range(3):                  # the same workspace: the counters restart at zero
+        out = _decode(P, wl, wl.k_pool, wl.v_pool, wl.ctx_after, workspace=ws)
+        assert report(f"claims rep {rep}", f32_of(out), want, wl.dtype) <= ATTN_TOL
