@@ -83,6 +83,24 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (N >= 16) x += dpp_f<DPP_ROW_MIRROR>(x);
   return x;
 }
+// group_sum of K independent values, one butterfly stage at a time over all of them: the DPP
+// reads of a stage then never wait on the result of the instruction just before them.
+template <int N, int K>
+__device__ __forceinline__ void group_sum_n(float (&x)[K]) {
+  static_assert(N == 4 || N == 8 || N == 16, "group of 4, 8 or 16 lanes");
+#pragma unroll
+  for (int k = 0; k < K; ++k) x[k] += dpp_f<DPP_QUAD_XOR1>(x[k]);
+#pragma unroll
+  for (int k = 0; k < K; ++k) x[k] += dpp_f<DPP_QUAD_XOR2>(x[k]);
+  if constexpr (N >= 8) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) x[k] += dpp_f<DPP_ROW_HALF_MIRROR>(x[k]);
+  }
+  if constexpr (N >= 16) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) x[k] += dpp_f<DPP_ROW_MIRROR>(x[k]);
+  }
+}
 template <int N>
 __device__ __forceinline__ float group_max(float x) {
   x = fmaxf(x, dpp_f<DPP_QUAD_XOR1>(x));

@@ -1,0 +1,697 @@
+// Paged decode attention (one query token per request), balanced split-K.
+//
+// What is computed ("Triton KV Cache and PagedAttention", Step 1 and the reference
+// answer, TODO 1-5): for request b and query head h, out = sum_t softmax_t(sm_scale *
+// q.k_t) v_t over the first context_lens[b] tokens; token t lives in physical block
+// block_tables[b, t / block_size] at slot t % block_size; tokens past the context are
+// masked; the softmax is accumulated online (running max m, running sum l, unnormalised
+// accumulator).  GQA ("Write Triton Kv Cache Append Kernel", Kernel design rules): the G =
+// Hq / Hkv query heads h = kvh*G .. kvh*G+G-1 share kv head kvh.  The 3-bit cache
+// ("triton-3bit-kv-cache-kernel" README, title paragraph and section 2) is unpacked and
+// dequantised, x = (q - z) * s, in registers.  Split-K: the context of a (request, kv head)
+// may be cut at multiples of the partition size into ranges that are reduced separately
+// and merged by log-sum-exp (the flash-decoding form the 3-bit README names).
+//
+// MI355X mapping:
+//  * Memory: one slot of a block stores all kv heads of a token contiguously
+//    ([block, slot, head, d]).  A wave instruction reads HPI heads x D elements of one
+//    token (1 KB for 4 heads of 128 bf16), and the waves of a workgroup cover the other
+//    heads of the same tokens at the same time, so whole slot rows are streamed and each
+//    opened DRAM page is used in full.  Lane layout: D/8 lanes per (head, token) row, each
+//    lane owning 8 consecutive elements (one 16-byte load of K and one of V).
+//  * Work (stream-K): requests are cut into granules of `partition_size` tokens; the
+//    (request, head group, granule) units are laid end to end and the grid holds as many
+//    workgroups as the chip keeps resident, each taking an equal contiguous range of
+//    units.  All workgroups stream for the same time, with no tail.  A (request, head
+//    group) segment covered by one workgroup is finished in registers; where a range starts
+//    or ends inside a segment the partial state (m, l, acc) goes to the workspace and a
+//    small second kernel merges it by log-sum-exp.
+//  * QK: v_dot2_f32_{bf16,f16} on packed pairs and a DPP reduction inside the lane row;
+//    each row keeps its own online-softmax state (m, l in log2 units, the lane's 8
+//    accumulator columns per query head).
+//  * Physical block ids of up to 64 chunks are fetched with one vector load (lane k <->
+//    k-th chunk) and read back with v_readlane; the next chunk's K/V loads are issued before
+//    the current chunk is computed (two register buffers).
+#pragma once
+#include <algorithm>
+#include <type_traits>
+
+#include "launch.h"
+#include "common.cuh"
+
+namespace pkv {
+
+constexpr int kMaxWaves = 8;        // waves per workgroup at most (token streams x head group)
+constexpr int kClaimWaves = 4;      // block counters per segment (one per head wave)
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
+
+__device__ __forceinline__ int clamp_ctx(const DecodeParams& p, int b) {
+  return min(max(p.context_lens[b], 0), p.max_context_len);
+}
+
+// Static split of the units over the grid.  The first workgroup dispatched to each CU is
+// issued ahead of the CU's later ones and streams faster, so the first `split_tier`
+// workgroups carry split_a / 16 of the share of the others: workgroup w starts at unit
+// floor(total * c(w) / c(W)) with c(w) = a * min(w, H) + 16 * max(0, w - H).
+__device__ __forceinline__ int64_t split_c(const DecodeParams& p, int64_t w) {
+  const int64_t h = p.split_tier;
+  return w <= h ? p.split_a * w : p.split_a * h + 16 * (w - h);
+}
+__device__ __forceinline__ int64_t range_start(const DecodeParams& p, int64_t total, int64_t w) {
+  return total * split_c(p, w) / split_c(p, p.num_wgs);
+}
+
+// Lane geometry for head_dim D with HPI heads per wave instruction (G query heads per kv head).
+template <int D, int HPI, int G>
+struct Geo {
+  static constexpr int LPR = D / 8;                 // lanes per (head, token) row
+  static constexpr int RPI = 64 / LPR;              // rows per wave instruction
+  static constexpr int TPI = RPI / HPI;             // tokens per wave instruction
+  static constexpr int NI = (16 / TPI) < 4 ? (16 / TPI) : 4;   // instructions per chunk
+  static constexpr int CT = NI * TPI;               // tokens per chunk (divides 16)
+  static_assert(RPI % HPI == 0 && 16 % CT == 0, "lane geometry");
+};
+
+template <int NI, CacheKind KIND> struct Regs;
+template <int NI> struct Regs<NI, CacheKind::Same> { uint4 k[NI], v[NI]; };
+template <int NI> struct Regs<NI, CacheKind::U3> {
+  uint32_t klo[NI], khi[NI], vlo[NI], vhi[NI], km[NI], vm[NI];
+};
+
+template <int G>
+struct State {
+  uint32_t qv[G][4];                 // this lane's 8 query elements of each query head
+  float qsum[G];                     // u3: sum of the query row (dequant hoisting)
+  float m[G], l[G], zc[G];
+  // accumulator column e (this lane's d = 8c + e) of query head g is acc4[g / 4][e][g % 4]: the
+  // register quads are the C operands of the PV matrix-core products
+  f32x4_t acc4[(G + 3) / 4][8];
+};
+
+#define PKV_ACC(S, g, e) ((S).acc4[(g) >> 2][e][(g) & 3])
+
+// acc[g][e] += w * p[g] * v[e] for the query heads g of this lane's row.  On the matrix cores:
+// v_mfma_f32_4x4x1f32 runs 16 independent 4x4 outer products per wave, block b taking
+// A[m] from lane 4b + m and B[n] from lane 4b + n and leaving C[m][n] in register m of lane
+// 4b + n.  The 4 lanes of a block lie in one (head, token) row (D/8 lanes, a multiple of 4),
+// all of which hold the row's p[g]; so with A = w * p[lane % 4] and B = v[e] of the lane
+// itself, register m of lane (row, c) gains w * p[m] * v[e], the same as the FMA form.
+// With G = 8 the extra operand registers push the kernel into spills (measured 7 % slower on
+// the long-context decode), so G = 8 keeps the FMA form.
+template <int G, typename St>
+__device__ __forceinline__ void pv_accumulate(St& S, const float (&p)[G], float w, const float (&v)[8]) {
+  if constexpr (G <= 4) {
+    const int q = threadIdx.x & 3;
+    float a = 0.f;                                  // heads g >= G of the quad stay 0
+#pragma unroll
+    for (int m = 0; m < G; ++m) a = (q == m) ? p[m] : a;
+    a *= w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) S.acc4[0][e] = __builtin_amdgcn_mfma_f32_4x4x1f32(a, v[e], S.acc4[0][e], 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float pw = p[g] * w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) PKV_ACC(S, g, e) = fmaf(pw, v[e], PKV_ACC(S, g, e));
+    }
+  }
+}
+
+// Per-lane byte offsets of the rows a lane reads in a chunk (instruction i reads the row
+// TPI*i slots after the lane's first row); the chunk's block and first slot are
+// wave-uniform and kept in scalar registers.
+template <int D, int HPI, CacheKind KIND, int G>
+struct LaneOffsets {
+  static constexpr int NI = Geo<D, HPI, G>::NI;
+  uint32_t row[NI];                  // bytes from the chunk's uniform row base
+  uint32_t meta[NI];                 // u3: bytes from the chunk's uniform meta base
+};
+
+template <int D, int HPI, CacheKind KIND, int G>
+__device__ __forceinline__ LaneOffsets<D, HPI, KIND, G> lane_offsets(const DecodeParams& p, int tr, int hh,
+                                                                   int c) {
+  using Gm = Geo<D, HPI, G>;
+  LaneOffsets<D, HPI, KIND, G> o;
+  constexpr int esz = KIND == CacheKind::U3 ? 4 : 2;
+  const int col = KIND == CacheKind::U3 ? ((3 * c) >> 2) : c * 8;
+#pragma unroll
+  for (int i = 0; i < Gm::NI; ++i) {
+    const int64_t slot = tr + i * Gm::TPI;
+    o.row[i] = (uint32_t)((slot * p.c_ss + (int64_t)hh * p.c_sh + col) * esz);
+    o.meta[i] = (uint32_t)((slot * p.num_kv_heads + hh) * 4);
+  }
+  return o;
+}
+
+// Issue the loads of one chunk: `kb`/`vb` point at the row of (block, first slot, first head
+// of the group) and `kmb`/`vmb` at its meta entry (u3), all wave-uniform.
+template <int D, int HPI, CacheKind KIND, int G>
+__device__ __forceinline__ void load_chunk(const char* kb, const char* vb, const char* kmb,
+                                           const char* vmb, const LaneOffsets<D, HPI, KIND, G>& o, int c,
+                                           Regs<Geo<D, HPI, G>::NI, KIND>& R) {
+  using Gm = Geo<D, HPI, G>;
+  if constexpr (KIND == CacheKind::Same) {
+#pragma unroll
+    for (int i = 0; i < Gm::NI; ++i) {
+      R.k[i] = *reinterpret_cast<const uint4*>(kb + o.row[i]);
+      R.v[i] = *reinterpret_cast<const uint4*>(vb + o.row[i]);
+    }
+  } else {
+    // 3-bit rows: D*3/32 words; lane c owns octet c = stream bits [24c, 24c + 24), which
+    // start in word 3c/4 and spill into the next word for c mod 4 in {1, 2}.
+    const bool two = ((c & 3) == 1) || ((c & 3) == 2);
+#pragma unroll
+    for (int i = 0; i < Gm::NI; ++i) {
+      R.klo[i] = *reinterpret_cast<const uint32_t*>(kb + o.row[i]);
+      R.khi[i] = two ? *reinterpret_cast<const uint32_t*>(kb + o.row[i] + 4) : 0u;
+      R.vlo[i] = *reinterpret_cast<const uint32_t*>(vb + o.row[i]);
+      R.vhi[i] = two ? *reinterpret_cast<const uint32_t*>(vb + o.row[i] + 4) : 0u;
+      R.km[i] = *reinterpret_cast<const uint32_t*>(kmb + o.meta[i]);
+      R.vm[i] = *reinterpret_cast<const uint32_t*>(vmb + o.meta[i]);
+    }
+  }
+}
+
+// QK, online-softmax update and PV for one chunk of this lane's row.  MASKED: tokens at or
+// past t_end are excluded (only the last chunk of a range can be ragged).
+template <int D, int G, bool BF16, CacheKind KIND, int HPI, bool MASKED>
+__device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S,
+                                              const Regs<Geo<D, HPI, G>::NI, KIND>& R, int tok,
+                                              int t_end, int c) {
+  using Gm = Geo<D, HPI, G>;
+  constexpr int NI = Gm::NI, LPR = Gm::LPR;
+  bool valid[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) valid[i] = !MASKED || (tok + i * Gm::TPI < t_end);
+  float sc[NI][G];
+  if constexpr (KIND == CacheKind::Same) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t kw[4] = {R.k[i].x, R.k[i].y, R.k[i].z, R.k[i].w};
+      float d[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        d[g] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[g] = dot2<BF16>(S.qv[g][e], kw[e], d[g]);
+      }
+      // stage-major across the query heads (no DPP read waits on the instruction before it);
+      // with 8 heads that schedule costs spills, so G = 8 reduces one value at a time
+      if constexpr (G <= 4) {
+        group_sum_n<LPR>(d);
+      } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g) d[g] = group_sum<LPR>(d[g]);
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) sc[i][g] = valid[i] ? d[g] * p.scale_log2 : neg_inf();
+    }
+  } else {
+    const int sh = (24 * c) & 31;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t ko = __builtin_amdgcn_alignbit(R.khi[i], R.klo[i], sh) & 0xffffffu;
+      // codes as packed 16-bit pairs: fp16 exactly (1024 + c, minus 1024); bf16 pairs keep a
+      // +128 offset that is folded into the zero point below
+      uint32_t cp[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t a = (ko >> (6 * e)) & 7u, bb = (ko >> (6 * e + 3)) & 7u;
+        if constexpr (BF16) {
+          cp[e] = (a | (bb << 16)) | 0x43004300u;
+        } else {
+          const uint32_t magic = (a | (bb << 16)) | 0x64006400u;
+          const f16x2_t v = __builtin_bit_cast(f16x2_t, magic) - (f16x2_t){1024.0f16, 1024.0f16};
+          cp[e] = __builtin_bit_cast(uint32_t, v);
+        }
+      }
+      float d[G];                      // (one value at a time: the stage-major schedule spills)
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        d[g] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[g] = dot2<BF16>(S.qv[g][e], cp[e], d[g]);
+        d[g] = group_sum<LPR>(d[g]);
+      }
+      const float ks = f16_lo(R.km[i]), kz = f16_hi(R.km[i]);
+      const float off = BF16 ? 128.f + kz : kz;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        // q.(code - z)*s = s * (q.code - z * sum(q))
+        sc[i][g] = valid[i] ? ks * (d[g] - off * S.qsum[g]) * p.scale_log2 : neg_inf();
+      }
+    }
+  }
+  // Online-softmax update.  The running maxima rarely grow once a few dozen tokens have been
+  // seen, so the rescaling of (l, acc) is skipped for the whole wave when no row's maximum
+  // grew in this chunk: the factor would be exp2(0) = 1 exactly, so the result is the same.
+  float pp[NI][G];
+  float mx[G];
+  bool grow = false;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    mx[g] = sc[0][g];
+#pragma unroll
+    for (int i = 1; i < NI; ++i) mx[g] = fmaxf(mx[g], sc[i][g]);
+    grow |= mx[g] > S.m[g];
+  }
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mn = fmaxf(S.m[g], mx[g]);
+      const float mu = (MASKED && mn == neg_inf()) ? 0.f : mn;   // a row with no token yet
+      const float al = fast_exp2(S.m[g] - mu);
+      S.m[g] = mn;
+      S.l[g] *= al;
+      if constexpr (KIND == CacheKind::U3) S.zc[g] *= al;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) PKV_ACC(S, g, e) *= al;
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float mu = (MASKED && S.m[g] == neg_inf()) ? 0.f : S.m[g];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      pp[i][g] = fast_exp2(sc[i][g] - mu);
+      S.l[g] += pp[i][g];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    float vf[8];
+    if constexpr (KIND == CacheKind::Same) {
+      uint32_t vw[4] = {R.v[i].x, R.v[i].y, R.v[i].z, R.v[i].w};
+      if (MASKED && !valid[i]) vw[0] = vw[1] = vw[2] = vw[3] = 0u;   // poisoned tails stay out
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vf[2 * e] = h_lo<BF16>(vw[e]);
+        vf[2 * e + 1] = h_hi<BF16>(vw[e]);
+      }
+      pv_accumulate<G>(S, pp[i], 1.f, vf);
+    } else {
+      const int sh = (24 * c) & 31;
+      const uint32_t vo = __builtin_amdgcn_alignbit(R.vhi[i], R.vlo[i], sh) & 0xffffffu;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vf[e] = (float)((vo >> (3 * e)) & 7u);
+      const float vs = valid[i] ? f16_lo(R.vm[i]) : 0.f;
+      const float vz = valid[i] ? f16_hi(R.vm[i]) : 0.f;
+      // sum_t p (code - z) s = sum_t (p s) code - sum_t (p s) z
+#pragma unroll
+      for (int g = 0; g < G; ++g) S.zc[g] = fmaf(pp[i][g] * vs, vz, S.zc[g]);
+      pv_accumulate<G>(S, pp[i], vs, vf);
+    }
+  }
+}
+
+// Reduce the chunks k = stream, stream + TS, ... of tokens [t0, t1) of request b, head group hg
+// into S (this lane's row: head hh of the group, token offset tr inside a wave instruction).
+template <int D, int G, bool BF16, CacheKind KIND, int HPI>
+__device__ __forceinline__ void run_range(const DecodeParams& p, State<G>& S, int b, int hg, int t0,
+                                          int t1, int lane, int tr, int hh, int c, int stream) {
+  using Gm = Geo<D, HPI, G>;
+  using R = Regs<Gm::NI, KIND>;
+  constexpr int esz = KIND == CacheKind::U3 ? 4 : 2;
+  const int nk = (t1 - t0 + Gm::CT - 1) / Gm::CT;
+  const bool ragged = ((t1 - t0) % Gm::CT) != 0;
+  const int32_t* bt_row = p.block_tables + b * p.bt_sb;
+  const int h_first = hg * p.heads_per_group;
+  const LaneOffsets<D, HPI, KIND, G> lo = lane_offsets<D, HPI, KIND, G>(p, tr, hh, c);
+  const char* kc = static_cast<const char*>(p.k_cache) + (int64_t)h_first * p.c_sh * esz;
+  const char* vc = static_cast<const char*>(p.v_cache) + (int64_t)h_first * p.c_sh * esz;
+  const char* kmc = static_cast<const char*>(p.k_meta) + (int64_t)h_first * 4;
+  const char* vmc = static_cast<const char*>(p.v_meta) + (int64_t)h_first * 4;
+  for (int win = 0; win < nk; win += 64) {
+    const int n = min(64, nk - win);
+    int bt_lane = 0;
+    if (lane < n) {
+      const int e = bt_row[(t0 + (win + lane) * Gm::CT) >> p.log2_bs];
+      bt_lane = (int)min<int64_t>(max(e, 0), p.num_blocks - 1);   // out-of-range ids clamped
+    }
+    auto issue = [&](int k, R& regs) {
+      const int tok0 = t0 + (win + k) * Gm::CT;
+      const int64_t phys = __builtin_amdgcn_readlane(bt_lane, k);
+      const int64_t slot0 = tok0 & (p.block_size - 1);
+      const int64_t rowb = (phys * p.c_sb + slot0 * p.c_ss) * esz;
+      const int64_t metab = ((phys * p.block_size + slot0) * p.num_kv_heads) * 4;
+      load_chunk<D, HPI, KIND, G>(kc + rowb, vc + rowb, kmc + metab, vmc + metab, lo, c, regs);
+    };
+    auto tok_of = [&](int k) { return t0 + (win + k) * Gm::CT + tr; };
+    // this stream's chunks k = first, first + ts, ... of the window; the ragged last chunk of
+    // the range is peeled off so that the loop body holds only the unmasked code, and the
+    // next chunk's loads are always in flight while the current one is computed
+    const int ts = p.token_streams;
+    const int n_plain = (ragged && win + n == nk) ? n - 1 : n;
+    int k = (stream - win % ts + ts) % ts;
+    if (k < n_plain) {
+      R ra, rb;
+      issue(k, ra);
+      for (;;) {
+        const int k1 = k + ts;
+        if (k1 < n_plain) issue(k1, rb);
+        compute_chunk<D, G, BF16, KIND, HPI, false>(p, S, ra, tok_of(k), t1, c);
+        k = k1;
+        if (k >= n_plain) break;
+        const int k2 = k + ts;
+        if (k2 < n_plain) issue(k2, ra);
+        compute_chunk<D, G, BF16, KIND, HPI, false>(p, S, rb, tok_of(k), t1, c);
+        k = k2;
+        if (k >= n_plain) break;
+      }
+    }
+    if (n_plain < n && k == n - 1) {
+      R regs;
+      issue(n - 1, regs);
+      compute_chunk<D, G, BF16, KIND, HPI, true>(p, S, regs, tok_of(n - 1), t1, c);
+    }
+  }
+}
+
+// The full blocks [0, nbf) of a segment shared by several workgroups, handed out one block at
+// a time to each wave from a counter of the segment in the workspace (one counter per head
+// wave, shared by that head wave's token streams in every sharing workgroup): whichever wave is
+// ready takes the next block, so the sharers, which run on different XCDs at different speeds,
+// finish the segment together instead of each finishing a fixed share.  Per wave, with no
+// barrier: lane 0 claims one block ahead of the one being read, the block id comes through the
+// scalar cache (so its wait never drains the vector loads), and the next block's first chunk is
+// issued before the current block's last chunk is computed.  A wave reads all `my_n` chunks of
+// each block it claims (an even count).
+template <int D, int G, bool BF16, CacheKind KIND, int HPI>
+__device__ __forceinline__ void run_claimed(const DecodeParams& p, State<G>& S, int b, int hg, int nbf,
+                                            int* claim, int lane, int tr, int hh, int c, int stream) {
+  using Gm = Geo<D, HPI, G>;
+  using R = Regs<Gm::NI, KIND>;
+  constexpr int esz = KIND == CacheKind::U3 ? 4 : 2;
+  const int my_n = p.block_size / Gm::CT;                 // chunks per block
+  typedef const __attribute__((address_space(4))) int32_t* ConstIntPtr;
+  const ConstIntPtr bt_row = (ConstIntPtr)(p.block_tables + b * p.bt_sb);
+  const int h_first = hg * p.heads_per_group;
+  const LaneOffsets<D, HPI, KIND, G> lo = lane_offsets<D, HPI, KIND, G>(p, tr, hh, c);
+  const char* kc = static_cast<const char*>(p.k_cache) + (int64_t)h_first * p.c_sh * esz;
+  const char* vc = static_cast<const char*>(p.v_cache) + (int64_t)h_first * p.c_sh * esz;
+  const char* kmc = static_cast<const char*>(p.k_meta) + (int64_t)h_first * 4;
+  const char* vmc = static_cast<const char*>(p.v_meta) + (int64_t)h_first * 4;
+  // a claim outside [0, nbf) ends the loop: a counter that is not zero at the start of the call
+  // (a workspace that was not zero-filled) can only lose work, never read outside the segment
+  auto take = [&](int v) { return (unsigned)v < (unsigned)nbf ? v : nbf; };
+  auto claim_async = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(claim, 1);
+    return v;
+  };
+  auto phys_of = [&](int u) {
+    return u < nbf ? (int64_t)min<int64_t>(max(bt_row[u], 0), p.num_blocks - 1) : (int64_t)0;
+  };
+  auto issue = [&](int64_t phys, int k, R& regs) {          // chunk k (in tokens k * CT) of a block
+    const int64_t slot0 = k * Gm::CT;
+    const int64_t rowb = (phys * p.c_sb + slot0 * p.c_ss) * esz;
+    const int64_t metab = ((phys * p.block_size + slot0) * p.num_kv_heads) * 4;
+    load_chunk<D, HPI, KIND, G>(kc + rowb, vc + rowb, kmc + metab, vmc + metab, lo, c, regs);
+  };
+  int uc = take(__builtin_amdgcn_readfirstlane(claim_async()));
+  int un = take(__builtin_amdgcn_readfirstlane(claim_async()));
+  int64_t pc = phys_of(uc);
+  R ra, rb;
+  if (uc < nbf) issue(pc, 0, ra);
+  while (uc < nbf) {
+    const int pending = (un < nbf) ? claim_async() : 0;   // the claim after next
+    const int64_t pn = phys_of(un);
+    for (int k = 0; k < my_n; k += 2) {
+      issue(pc, k + 1, rb);
+      compute_chunk<D, G, BF16, KIND, HPI, false>(p, S, ra, uc * p.block_size + k * Gm::CT + tr, 0, c);
+      if (k + 2 < my_n) issue(pc, k + 2, ra);
+      else if (un < nbf) issue(pn, 0, ra);
+      compute_chunk<D, G, BF16, KIND, HPI, false>(p, S, rb, uc * p.block_size + (k + 1) * Gm::CT + tr, 0, c);
+    }
+    uc = un;
+    pc = pn;
+    un = (un < nbf) ? take(__builtin_amdgcn_readfirstlane(pending)) : nbf;
+  }
+}
+
+// Merge the rows of the wave that hold the same head at different token offsets (TPI > 1).
+template <int D, int G, CacheKind KIND, int HPI>
+__device__ __forceinline__ void merge_rows(State<G>& S) {
+  using Gm = Geo<D, HPI, G>;
+  if constexpr (KIND == CacheKind::U3) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) PKV_ACC(S, g, e) -= S.zc[g];
+  }
+#pragma unroll
+  for (int off = HPI * Gm::LPR; off < 64; off <<= 1) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mo = __shfl_xor(S.m[g], off);
+      const float lo = __shfl_xor(S.l[g], off);
+      const float mn = fmaxf(S.m[g], mo);
+      const float mu = (mn == neg_inf()) ? 0.f : mn;
+      const float fs = fast_exp2(S.m[g] - mu), fo = fast_exp2(mo - mu);
+      S.l[g] = S.l[g] * fs + lo * fo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float ao = __shfl_xor(PKV_ACC(S, g, e), off);
+        PKV_ACC(S, g, e) = PKV_ACC(S, g, e) * fs + ao * fo;
+      }
+      S.m[g] = mn;
+    }
+  }
+}
+
+// s_pref[i] = granules of requests 0..i-1 (i = 0..B), from the (clamped) context lengths.
+__device__ void build_prefix(const DecodeParams& p, int* s_pref, int* s_tile) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nwv = blockDim.x >> 6;
+  int carry = 0;
+  for (int base = 0; base < p.batch; base += blockDim.x) {
+    const int i = base + threadIdx.x;
+    int x = 0;
+    if (i < p.batch) x = (clamp_ctx(p, i) + p.partition_size - 1) / p.partition_size;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) s_tile[w] = x;
+    __syncthreads();
+    int before = carry, total = carry;
+    for (int j = 0; j < nwv; ++j) {
+      if (j < w) before += s_tile[j];
+      total += s_tile[j];
+    }
+    if (i < p.batch) s_pref[i + 1] = before + x;
+    carry = total;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) s_pref[0] = 0;
+  __syncthreads();
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_out_row(const DecodeParams& p, int b, int h, int c,
+                                              const float (&a)[8], float inv_l) {
+  uint4 o;
+  o.x = pack2<BF16>(a[0] * inv_l, a[1] * inv_l);
+  o.y = pack2<BF16>(a[2] * inv_l, a[3] * inv_l);
+  o.z = pack2<BF16>(a[4] * inv_l, a[5] * inv_l);
+  o.w = pack2<BF16>(a[6] * inv_l, a[7] * inv_l);
+  *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + b * p.o_sb + (int64_t)h * p.o_sh + c * 8) = o;
+}
+
+// CLAIM: compiled with the run-time block hand-out of shared segments (p.claim_blocks set).
+// Kept out of the other instances so that its extra live state costs them no registers.
+template <int D, int G, bool BF16, CacheKind KIND, int HPI, bool CLAIM>
+__global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) {
+  using Gm = Geo<D, HPI, G>;
+  extern __shared__ int s_pref[];              // batch + 1 entries
+  __shared__ int s_tile[kMaxWaves];
+  build_prefix(p, s_pref, s_tile);
+
+  const int lane = threadIdx.x & 63;
+  const int hw_count = p.heads_per_group / HPI;  // waves per token stream
+  const int wv = (threadIdx.x >> 6) % hw_count;  // wave inside the token stream
+  const int stream = (threadIdx.x >> 6) / hw_count;
+  const int r = lane / Gm::LPR;
+  const int c = lane % Gm::LPR;
+  const int hr = r % HPI;                       // head of the row inside the instruction
+  const int tr = r / HPI;                       // token offset of the row
+  // token streams 1.. hand their per-segment state to stream 0 through LDS:
+  // [stream - 1][head in group][query head][D accumulators, m, l]
+  float* s_x = reinterpret_cast<float*>(s_pref + ((p.batch + 1 + 3) & ~3));
+  const int64_t NHG = p.num_head_groups;
+  const int64_t total = NHG * s_pref[p.batch];            // units of all segments
+  const int64_t wg = blockIdx.x;
+  int64_t x = range_start(p, total, wg);
+  const int64_t x_end = range_start(p, total, wg + 1);
+  if (x == x_end) {            // empty range (fewer units than workgroups): an empty state in slot 0
+    const int n_st = p.heads_per_group * G;
+    for (int i = threadIdx.x; i < n_st * D; i += blockDim.x) p.ws_acc[(wg * 2 * n_st) * D + i] = 0.f;
+    for (int i = threadIdx.x; i < n_st; i += blockDim.x)
+      *reinterpret_cast<float2*>(p.ws_ml + (wg * 2 * n_st + i) * 2) = make_float2(neg_inf(), 0.f);
+    return;
+  }
+  bool first = true;
+  while (x < x_end) {
+    // segment (request b, head group hg) holding unit x: the last b with NHG*s_pref[b] <= x
+    int lo = 0, hi = p.batch;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (NHG * s_pref[mid] <= x) lo = mid; else hi = mid;
+    }
+    const int b = lo;
+    const int n = s_pref[b + 1] - s_pref[b];
+    const int64_t off = x - NHG * s_pref[b];
+    const int hg = (int)(off / n);
+    const int g0 = (int)(off - (int64_t)hg * n);
+    const int g1 = (int)min<int64_t>(n, g0 + (x_end - x));
+    const int ctx = clamp_ctx(p, b);
+    if (threadIdx.x == 0) {                    // where the merge kernel finds this segment's pieces
+      const int64_t sidx = (int64_t)b * NHG + hg;
+      if (g0 == 0) p.ws_seg[2 * sidx] = (int)(wg * 2 + (first ? 0 : 1));
+      if (g1 == n) p.ws_seg[2 * sidx + 1] = (int)wg;
+    }
+    const int t0 = g0 * p.partition_size;
+    const int t1 = min(ctx, g1 * p.partition_size);
+    const int hh = wv * HPI + hr;                          // head inside the group
+    const int h = hg * p.heads_per_group + hh;             // kv head of this lane's row
+
+    State<G> S;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) +
+                                                      b * p.q_sb + (int64_t)(h * G + g) * p.q_sh + c * 8);
+      S.qv[g][0] = v.x; S.qv[g][1] = v.y; S.qv[g][2] = v.z; S.qv[g][3] = v.w;
+      S.qsum[g] = 0.f;
+      if constexpr (KIND == CacheKind::U3) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s += h_lo<BF16>(S.qv[g][e]) + h_hi<BF16>(S.qv[g][e]);
+        S.qsum[g] = group_sum<Gm::LPR>(s);
+      }
+      S.m[g] = neg_inf();
+      S.l[g] = 0.f;
+      S.zc[g] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) PKV_ACC(S, g, e) = 0.f;
+    }
+    if constexpr (CLAIM) {
+      if (!(g0 == 0 && g1 == n)) {
+        // a shared segment: its full blocks by claim; the ragged tail (if any) by the workgroup
+        // that holds the segment's last unit
+        const int nbf = ctx >> p.log2_bs;
+        run_claimed<D, G, BF16, KIND, HPI>(p, S, b, hg, nbf,
+                                           p.ws_claim + ((int64_t)b * NHG + hg) * kClaimWaves + wv,
+                                           lane, tr, hh, c, stream);
+        if (g1 == n && (nbf << p.log2_bs) < ctx)
+          run_range<D, G, BF16, KIND, HPI>(p, S, b, hg, nbf << p.log2_bs, ctx, lane, tr, hh, c, stream);
+      } else {
+        run_range<D, G, BF16, KIND, HPI>(p, S, b, hg, t0, t1, lane, tr, hh, c, stream);
+      }
+    } else {
+      run_range<D, G, BF16, KIND, HPI>(p, S, b, hg, t0, t1, lane, tr, hh, c, stream);
+    }
+    merge_rows<D, G, KIND, HPI>(S);
+    if (p.token_streams > 1) {
+      if (stream > 0 && tr == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float* xs = s_x + (((int64_t)(stream - 1) * p.heads_per_group + hh) * G + g) * (D + 2);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xs[c * 8 + e] = PKV_ACC(S, g, e);
+          if (c == 0) {
+            xs[D] = S.m[g];
+            xs[D + 1] = S.l[g];
+          }
+        }
+      }
+      __syncthreads();
+      if (stream == 0) {
+        for (int q = 1; q < p.token_streams; ++q) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float* xs = s_x + (((int64_t)(q - 1) * p.heads_per_group + hh) * G + g) * (D + 2);
+            const float mo = xs[D], lo2 = xs[D + 1];
+            const float mn = fmaxf(S.m[g], mo);
+            const float mu = (mn == neg_inf()) ? 0.f : mn;
+            const float fs = fast_exp2(S.m[g] - mu), fo = fast_exp2(mo - mu);
+            S.l[g] = S.l[g] * fs + lo2 * fo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) PKV_ACC(S, g, e) = PKV_ACC(S, g, e) * fs + xs[c * 8 + e] * fo;
+            S.m[g] = mn;
+          }
+        }
+      }
+      __syncthreads();                          // the buffer is reused by the next segment
+    }
+    if (stream == 0 && tr == 0) {
+      if (g0 == 0 && g1 == n) {                   // whole segment: final output
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float a8[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a8[e] = PKV_ACC(S, g, e);
+          store_out_row<BF16>(p, b, h * G + g, c, a8, 1.f / S.l[g]);
+        }
+      } else {                                    // part of a split segment
+        const int64_t slot = (wg * 2 + (first ? 0 : 1)) * p.heads_per_group + hh;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float* dst = p.ws_acc + (slot * G + g) * D + c * 8;
+          *reinterpret_cast<float4*>(dst) = make_float4(PKV_ACC(S, g, 0), PKV_ACC(S, g, 1), PKV_ACC(S, g, 2), PKV_ACC(S, g, 3));
+          *reinterpret_cast<float4*>(dst + 4) = make_float4(PKV_ACC(S, g, 4), PKV_ACC(S, g, 5), PKV_ACC(S, g, 6), PKV_ACC(S, g, 7));
+          if (c == 0) *reinterpret_cast<float2*>(p.ws_ml + (slot * G + g) * 2) = make_float2(S.m[g], S.l[g]);
+        }
+      }
+    }
+    x += g1 - g0;
+    first = false;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Instance lookup.  The instances are compiled in four translation units (decode_same_d128,
+// decode_same_d64, decode_u3_d128, decode_u3_d64), each exporting the pointer lookup of its
+// head dim and cache kind, so that the build can compile them in parallel.
+// ---------------------------------------------------------------------------------------
+template <int D, int G, bool BF16, CacheKind KIND, int HPI>
+const void* kernel_ptr(bool claim) {
+  return claim ? reinterpret_cast<const void*>(&decode_kernel<D, G, BF16, KIND, HPI, true>)
+               : reinterpret_cast<const void*>(&decode_kernel<D, G, BF16, KIND, HPI, false>);
+}
+
+template <int D, int G, bool BF16, CacheKind KIND>
+const void* kernel_by_hpi(int hpi, bool claim) {
+  switch (hpi) {
+    case 1: return kernel_ptr<D, G, BF16, KIND, 1>(claim);
+    case 2: return kernel_ptr<D, G, BF16, KIND, 2>(claim);
+    case 4: return kernel_ptr<D, G, BF16, KIND, 4>(claim);
+    case 8: if constexpr (D == 64) return kernel_ptr<D, G, BF16, KIND, 8>(claim); else return nullptr;
+  }
+  return nullptr;
+}
+
+template <int D, bool BF16, CacheKind KIND>
+const void* kernel_by_g(int group, int hpi, bool claim) {
+  switch (group) {
+    case 1: return kernel_by_hpi<D, 1, BF16, KIND>(hpi, claim);
+    case 2: return kernel_by_hpi<D, 2, BF16, KIND>(hpi, claim);
+    case 4: return kernel_by_hpi<D, 4, BF16, KIND>(hpi, claim);
+    case 8: return kernel_by_hpi<D, 8, BF16, KIND>(hpi, claim);
+  }
+  return nullptr;
+}
+
+template <int D, CacheKind KIND>
+const void* kernel_by_dtype(int group, bool bf16, int hpi, bool claim) {
+  return bf16 ? kernel_by_g<D, true, KIND>(group, hpi, claim) : kernel_by_g<D, false, KIND>(group, hpi, claim);
+}
+
+// host pointer of decode_kernel<D, group, bf16, KIND, hpi, claim>, or nullptr if not built
+const void* decode_kernel_ptr_same_d128(int group, bool bf16, int hpi, bool claim);
+const void* decode_kernel_ptr_same_d64(int group, bool bf16, int hpi, bool claim);
+const void* decode_kernel_ptr_u3_d128(int group, bool bf16, int hpi, bool claim);
+const void* decode_kernel_ptr_u3_d64(int group, bool bf16, int hpi, bool claim);
+
+}  // namespace pkv
