@@ -46,6 +46,13 @@ constexpr int kMaxBatch = 8192;       // the decode kernel keeps batch + 1 prefi
 // with two resident workgroups per CU the first one streams ~1.17x faster (measured on the
 // Llama-8B decode step, 86.6 vs 101.6 us mean), and 22/16 evened the tiers out best.
 constexpr int kFirstTierWeight = 22;
+// run-time hand-out of shared segments: from this many bytes of K/V per wave and block, in
+// units of this many chunks (0: whole blocks)
+constexpr int64_t kClaimMinBlockBytes = 64 * 1024;
+constexpr int kClaimUnitChunks = 0;
+// a workgroup that starts a segment inside its range first waits for the segment's context
+// length, q and block table: charged to the static split as this many tokens of work
+constexpr int kSegmentStartTokens = 16;
 // Block counters kept at the head of every decode workspace (4 per (request, kv-head group)
 // segment); calls with more segments use the static split only.
 constexpr size_t kClaimSlots = 65536;
@@ -269,6 +276,7 @@ int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
   p.num_wgs = L.plan.num_wgs;
   p.split_tier = L.plan.split_tier;
   p.split_a = kFirstTierWeight;
+  p.seg_start_units = (kSegmentStartTokens + ps / 2) / ps;
   p.heads_per_group = L.plan.heads_per_group;
   p.num_head_groups = L.plan.num_head_groups;
   p.token_streams = L.plan.token_streams;
@@ -286,9 +294,13 @@ int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
   // needs an even number of chunks per block and at most 4 head waves.
   const int64_t row_bytes = cache_dtype == PKV_U3 ? 2 * (head_dim * 3 / 8 + 4) : 4 * (int64_t)head_dim;
   const int64_t wave_block_bytes = (int64_t)block_size * L.plan.hpi * row_bytes;
-  p.claim_blocks = (wave_block_bytes >= 64 * 1024 && block_size % (L.plan.chunk_tokens * 2) == 0 &&
-                    L.plan.heads_per_group / L.plan.hpi <= 4 &&
-                    (size_t)batch * L.plan.num_head_groups * 4 <= kClaimSlots) ? 1 : 0;
+  const int unit_tokens = kClaimUnitChunks > 0 ? std::min(block_size, kClaimUnitChunks * L.plan.chunk_tokens)
+                                               : block_size;
+  p.claim_units = (wave_block_bytes >= kClaimMinBlockBytes && unit_tokens % (L.plan.chunk_tokens * 2) == 0 &&
+                   L.plan.heads_per_group / L.plan.hpi <= 4 &&
+                   (size_t)batch * L.plan.num_head_groups * 4 <= kClaimSlots) ? 1 : 0;
+  p.log2_claim = 0;
+  while ((1 << p.log2_claim) < unit_tokens) ++p.log2_claim;
   const hipError_t e = pkv::launch_decode(p, L.plan, kind, q_dtype == PKV_BF16, head_dim, group, stream);
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
 }

@@ -24,7 +24,7 @@ __global__ __launch_bounds__(D * kMergeMaxSplit) void merge_kernel(DecodeParams 
   const int d = threadIdx.x % D, part = threadIdx.x / D;
   uint16_t* out = static_cast<uint16_t*>(p.out) + b * p.o_sb + (int64_t)(kvh * G + g) * p.o_sh;
   // the decode kernel has finished: leave the segment's block counters at zero for the next call
-  if (p.claim_blocks && hh == 0 && g == 0 && threadIdx.x < kClaimWaves)
+  if (p.claim_units && hh == 0 && g == 0 && threadIdx.x < kClaimWaves)
     p.ws_claim[((int64_t)b * p.num_head_groups + hg) * kClaimWaves + threadIdx.x] = 0;
   if (clamp_ctx(p, b) == 0) {
     if (part == 0) out[d] = 0;
@@ -169,7 +169,7 @@ DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int head_di
 hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan, CacheKind kind, bool bf16,
                          int head_dim, int group, hipStream_t s) {
   if (p.batch == 0) return hipSuccess;
-  const void* fn = decode_kernel_ptr(head_dim, group, bf16, kind, plan.hpi, p.claim_blocks != 0);
+  const void* fn = decode_kernel_ptr(head_dim, group, bf16, kind, plan.hpi, p.claim_units != 0);
   const void* mf = merge_kernel_ptr(head_dim, group, bf16);
   if (!fn || !mf) return hipErrorInvalidValue;
   void* args[] = {const_cast<DecodeParams*>(&p)};

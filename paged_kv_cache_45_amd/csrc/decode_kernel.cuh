@@ -369,22 +369,23 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, State<G>& S, in
   }
 }
 
-// The full blocks [0, nbf) of a segment shared by several workgroups, handed out one block at
-// a time to each wave from a counter of the segment in the workspace (one counter per head
-// wave, shared by that head wave's token streams in every sharing workgroup): whichever wave is
-// ready takes the next block, so the sharers, which run on different XCDs at different speeds,
-// finish the segment together instead of each finishing a fixed share.  Per wave, with no
-// barrier: lane 0 claims one block ahead of the one being read, the block id comes through the
-// scalar cache (so its wait never drains the vector loads), and the next block's first chunk is
-// issued before the current block's last chunk is computed.  A wave reads all `my_n` chunks of
-// each block it claims (an even count).
+// The full claim units [0, nu) of a segment shared by several workgroups (unit u = tokens
+// [u * UT, u * UT + UT), UT = 2^log2_ut tokens inside one block), handed out one unit at a time
+// to each wave from a counter of the segment in the workspace (one counter per head wave,
+// shared by that head wave's token streams in every sharing workgroup): whichever wave is ready
+// takes the next unit, so the sharers, which run on different XCDs at different speeds, finish
+// the segment together instead of each finishing a fixed share.  Per wave, with no barrier:
+// lane 0 claims one unit ahead of the one being read, the block id comes through the scalar
+// cache (so its wait never drains the vector loads), and the next unit's first chunk is issued
+// before the current unit's last chunk is computed.  A wave reads all chunks of each unit it
+// claims (an even count).
 template <int D, int G, bool BF16, CacheKind KIND, int HPI>
-__device__ __forceinline__ void run_claimed(const DecodeParams& p, State<G>& S, int b, int hg, int nbf,
+__device__ __forceinline__ void run_claimed(const DecodeParams& p, State<G>& S, int b, int hg, int nu,
                                             int* claim, int lane, int tr, int hh, int c, int stream) {
   using Gm = Geo<D, HPI, G>;
   using R = Regs<Gm::NI, KIND>;
   constexpr int esz = KIND == CacheKind::U3 ? 4 : 2;
-  const int my_n = p.block_size / Gm::CT;                 // chunks per block
+  const int my_n = (1 << p.log2_claim) / Gm::CT;          // chunks per unit
   typedef const __attribute__((address_space(4))) int32_t* ConstIntPtr;
   const ConstIntPtr bt_row = (ConstIntPtr)(p.block_tables + b * p.bt_sb);
   const int h_first = hg * p.heads_per_group;
@@ -393,41 +394,50 @@ __device__ __forceinline__ void run_claimed(const DecodeParams& p, State<G>& S, 
   const char* vc = static_cast<const char*>(p.v_cache) + (int64_t)h_first * p.c_sh * esz;
   const char* kmc = static_cast<const char*>(p.k_meta) + (int64_t)h_first * 4;
   const char* vmc = static_cast<const char*>(p.v_meta) + (int64_t)h_first * 4;
-  // a claim outside [0, nbf) ends the loop: a counter that is not zero at the start of the call
+  // a claim outside [0, nu) ends the loop: a counter that is not zero at the start of the call
   // (a workspace that was not zero-filled) can only lose work, never read outside the segment
-  auto take = [&](int v) { return (unsigned)v < (unsigned)nbf ? v : nbf; };
+  auto take = [&](int v) { return (unsigned)v < (unsigned)nu ? v : nu; };
   auto claim_async = [&]() {
     int v = 0;
     if (lane == 0) v = atomicAdd(claim, 1);
     return v;
   };
-  auto phys_of = [&](int u) {
-    return u < nbf ? (int64_t)min<int64_t>(max(bt_row[u], 0), p.num_blocks - 1) : (int64_t)0;
+  // unit u's block (id through the scalar cache) and first slot in it
+  struct Loc { int64_t phys; int slot; };
+  auto loc_of = [&](int u) {
+    Loc l{0, 0};
+    if (u < nu) {
+      const int t = u << p.log2_claim;
+      l.phys = min<int64_t>(max(bt_row[t >> p.log2_bs], 0), p.num_blocks - 1);
+      l.slot = t & (p.block_size - 1);
+    }
+    return l;
   };
-  auto issue = [&](int64_t phys, int k, R& regs) {          // chunk k (in tokens k * CT) of a block
-    const int64_t slot0 = k * Gm::CT;
-    const int64_t rowb = (phys * p.c_sb + slot0 * p.c_ss) * esz;
-    const int64_t metab = ((phys * p.block_size + slot0) * p.num_kv_heads) * 4;
+  auto issue = [&](const Loc& l, int k, R& regs) {         // chunk k (tokens k * CT) of a unit
+    const int64_t slot0 = l.slot + k * Gm::CT;
+    const int64_t rowb = (l.phys * p.c_sb + slot0 * p.c_ss) * esz;
+    const int64_t metab = ((l.phys * p.block_size + slot0) * p.num_kv_heads) * 4;
     load_chunk<D, HPI, KIND, G>(kc + rowb, vc + rowb, kmc + metab, vmc + metab, lo, c, regs);
   };
   int uc = take(__builtin_amdgcn_readfirstlane(claim_async()));
   int un = take(__builtin_amdgcn_readfirstlane(claim_async()));
-  int64_t pc = phys_of(uc);
+  Loc pc = loc_of(uc);
   R ra, rb;
-  if (uc < nbf) issue(pc, 0, ra);
-  while (uc < nbf) {
-    const int pending = (un < nbf) ? claim_async() : 0;   // the claim after next
-    const int64_t pn = phys_of(un);
+  if (uc < nu) issue(pc, 0, ra);
+  while (uc < nu) {
+    const int pending = (un < nu) ? claim_async() : 0;    // the claim after next
+    const Loc pn = loc_of(un);
+    const int tok = (uc << p.log2_claim) + tr;
     for (int k = 0; k < my_n; k += 2) {
       issue(pc, k + 1, rb);
-      compute_chunk<D, G, BF16, KIND, HPI, false>(p, S, ra, uc * p.block_size + k * Gm::CT + tr, 0, c);
+      compute_chunk<D, G, BF16, KIND, HPI, false>(p, S, ra, tok + k * Gm::CT, 0, c);
       if (k + 2 < my_n) issue(pc, k + 2, ra);
-      else if (un < nbf) issue(pn, 0, ra);
-      compute_chunk<D, G, BF16, KIND, HPI, false>(p, S, rb, uc * p.block_size + (k + 1) * Gm::CT + tr, 0, c);
+      else if (un < nu) issue(pn, 0, ra);
+      compute_chunk<D, G, BF16, KIND, HPI, false>(p, S, rb, tok + (k + 1) * Gm::CT, 0, c);
     }
     uc = un;
     pc = pn;
-    un = (un < nbf) ? take(__builtin_amdgcn_readfirstlane(pending)) : nbf;
+    un = (un < nu) ? take(__builtin_amdgcn_readfirstlane(pending)) : nu;
   }
 }
 
@@ -461,7 +471,9 @@ __device__ __forceinline__ void merge_rows(State<G>& S) {
   }
 }
 
-// s_pref[i] = granules of requests 0..i-1 (i = 0..B), from the (clamped) context lengths.
+// s_pref[i] = units of requests 0..i-1 (i = 0..B): a non-empty request has its granules plus
+// seg_start_units units that hold no tokens, so that the static split charges the start of a
+// segment (context length, q and block-table loads ahead of the first K/V) like work.
 __device__ void build_prefix(const DecodeParams& p, int* s_pref, int* s_tile) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nwv = blockDim.x >> 6;
   int carry = 0;
@@ -469,6 +481,7 @@ __device__ void build_prefix(const DecodeParams& p, int* s_pref, int* s_tile) {
     const int i = base + threadIdx.x;
     int x = 0;
     if (i < p.batch) x = (clamp_ctx(p, i) + p.partition_size - 1) / p.partition_size;
+    if (x > 0) x += p.seg_start_units;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int y = __shfl_up(x, off);
@@ -500,7 +513,7 @@ __device__ __forceinline__ void store_out_row(const DecodeParams& p, int b, int 
   *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + b * p.o_sb + (int64_t)h * p.o_sh + c * 8) = o;
 }
 
-// CLAIM: compiled with the run-time block hand-out of shared segments (p.claim_blocks set).
+// CLAIM: compiled with the run-time hand-out of shared segments (p.claim_units set).
 // Kept out of the other instances so that its extra live state costs them no registers.
 template <int D, int G, bool BF16, CacheKind KIND, int HPI, bool CLAIM>
 __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) {
@@ -552,8 +565,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
       if (g0 == 0) p.ws_seg[2 * sidx] = (int)(wg * 2 + (first ? 0 : 1));
       if (g1 == n) p.ws_seg[2 * sidx + 1] = (int)wg;
     }
-    const int t0 = g0 * p.partition_size;
-    const int t1 = min(ctx, g1 * p.partition_size);
+    const int t0 = max(g0 - p.seg_start_units, 0) * p.partition_size;   // start units: no tokens
+    const int t1 = min(ctx, max(g1 - p.seg_start_units, 0) * p.partition_size);
     const int hh = wv * HPI + hr;                          // head inside the group
     const int h = hg * p.heads_per_group + hh;             // kv head of this lane's row
 
@@ -578,14 +591,14 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
     }
     if constexpr (CLAIM) {
       if (!(g0 == 0 && g1 == n)) {
-        // a shared segment: its full blocks by claim; the ragged tail (if any) by the workgroup
-        // that holds the segment's last unit
-        const int nbf = ctx >> p.log2_bs;
-        run_claimed<D, G, BF16, KIND, HPI>(p, S, b, hg, nbf,
+        // a shared segment: its full claim units by claim; the ragged tail (if any) by the
+        // workgroup that holds the segment's last granule
+        const int nu = ctx >> p.log2_claim;
+        run_claimed<D, G, BF16, KIND, HPI>(p, S, b, hg, nu,
                                            p.ws_claim + ((int64_t)b * NHG + hg) * kClaimWaves + wv,
                                            lane, tr, hh, c, stream);
-        if (g1 == n && (nbf << p.log2_bs) < ctx)
-          run_range<D, G, BF16, KIND, HPI>(p, S, b, hg, nbf << p.log2_bs, ctx, lane, tr, hh, c, stream);
+        if (g1 == n && (nu << p.log2_claim) < ctx)
+          run_range<D, G, BF16, KIND, HPI>(p, S, b, hg, nu << p.log2_claim, ctx, lane, tr, hh, c, stream);
       } else {
         run_range<D, G, BF16, KIND, HPI>(p, S, b, hg, t0, t1, lane, tr, hh, c, stream);
       }

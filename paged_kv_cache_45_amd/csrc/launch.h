@@ -42,6 +42,7 @@ struct DecodeParams {
   int64_t num_blocks;                 // block-table entries are clamped into [0, num_blocks)
   int max_context_len;                // context lengths are clamped into [0, max_context_len]
   int partition_size;                 // split granule in tokens, multiple of 16
+  int seg_start_units;                // units without tokens ahead of each non-empty segment
   int64_t num_wgs;                    // workgroups in the decode grid
   int64_t split_tier;                 // workgroups of the first dispatch tier (one per CU)
   int64_t split_a;                    // their share of the units relative to the rest, in 1/16
@@ -52,8 +53,9 @@ struct DecodeParams {
   float* ws_acc;                      // [num_wgs, 2, heads_per_group, G, D] partial accumulators
   float* ws_ml;                       // [num_wgs, 2, heads_per_group, G, 2] partial (m, l)
   int* ws_seg;                        // [batch, head groups, 2] first partial slot, last owner
-  int* ws_claim;                      // [batch, head groups, 4] block counters (zero between calls)
-  int claim_blocks;                   // shared segments hand out their blocks dynamically
+  int* ws_claim;                      // [batch, head groups, 4] unit counters (zero between calls)
+  int claim_units;                    // shared segments hand out their tokens dynamically ...
+  int log2_claim;                     // ... in units of 2^log2_claim tokens inside one block
 };
 
 // Launch geometry of paged_decode.
