@@ -42,10 +42,20 @@ int resolve_partition(int partition_size, int max_context_len, int batch, int nu
 
 constexpr int kMaxPartition = 1 << 20;
 constexpr int kMaxBatch = 8192;       // the decode kernel keeps batch + 1 prefix sums in LDS
-// Share of the units given to the first workgroup on each CU, in 1/16 of the others' share:
-// with two resident workgroups per CU the first one streams ~1.17x faster (measured on the
-// Llama-8B decode step, 86.6 vs 101.6 us mean), and 22/16 evened the tiers out best.
-constexpr int kFirstTierWeight = 22;
+// Static split weights (units share of a workgroup, in 1/64), by dispatch tier (the first
+// workgroup on each CU streams ahead of the CU's later ones) and by the parity of its XCD
+// (workgroup w runs on XCD w mod 8; per-workgroup traces of the Llama-8B step showed the
+// odd-numbered XCDs ending 5 % later on average, on three machines).  Measured, three
+// interleaved runs each:
+//  * static split, bf16/fp16 cache (HBM-bound): first tier 96 (24/16), odd 61 against 88 / 64:
+//    Llama-8B step 0.602 -> 0.607 of HBM peak;
+//  * static split, 3-bit cache (VALU-bound, so the XCDs' memory paths do not matter): first
+//    tier 96 helps (+0.4 %), the odd-XCD weight costs 1 %;
+//  * run-time block hand-out (long context): 88 / 64; 96 costs 3 %.
+struct SplitWeights { int64_t first_even, first_odd, rest_even, rest_odd; };
+constexpr SplitWeights kSplitStatic{96, 92, 64, 61};
+constexpr SplitWeights kSplitStaticU3{96, 96, 64, 64};
+constexpr SplitWeights kSplitClaimed{88, 88, 64, 64};
 // run-time hand-out of shared segments: from this many bytes of K/V per wave and block, in
 // units of this many chunks (0: whole blocks)
 constexpr int64_t kClaimMinBlockBytes = 64 * 1024;
@@ -275,7 +285,6 @@ int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
   p.partition_size = ps;
   p.num_wgs = L.plan.num_wgs;
   p.split_tier = L.plan.split_tier;
-  p.split_a = kFirstTierWeight;
   p.seg_start_units = (kSegmentStartTokens + ps / 2) / ps;
   p.heads_per_group = L.plan.heads_per_group;
   p.num_head_groups = L.plan.num_head_groups;
@@ -301,6 +310,11 @@ int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
                    (size_t)batch * L.plan.num_head_groups * 4 <= kClaimSlots) ? 1 : 0;
   p.log2_claim = 0;
   while ((1 << p.log2_claim) < unit_tokens) ++p.log2_claim;
+  const SplitWeights sw = p.claim_units ? kSplitClaimed : cache_dtype == PKV_U3 ? kSplitStaticU3 : kSplitStatic;
+  p.split_w[0] = sw.first_even;
+  p.split_w[1] = sw.first_odd;
+  p.split_w[2] = sw.rest_even;
+  p.split_w[3] = sw.rest_odd;
   const hipError_t e = pkv::launch_decode(p, L.plan, kind, q_dtype == PKV_BF16, head_dim, group, stream);
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
 }

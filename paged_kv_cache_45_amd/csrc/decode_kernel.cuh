@@ -50,13 +50,19 @@ __device__ __forceinline__ int clamp_ctx(const DecodeParams& p, int b) {
   return min(max(p.context_lens[b], 0), p.max_context_len);
 }
 
-// Static split of the units over the grid.  The first workgroup dispatched to each CU is
-// issued ahead of the CU's later ones and streams faster, so the first `split_tier`
-// workgroups carry split_a / 16 of the share of the others: workgroup w starts at unit
-// floor(total * c(w) / c(W)) with c(w) = a * min(w, H) + 16 * max(0, w - H).
+// Static split of the units over the grid.  Workgroup w carries a share proportional to a
+// weight that depends on its dispatch tier and on the parity of w: the first workgroup
+// dispatched to each CU (w < split_tier) is issued ahead of the CU's later ones and streams
+// faster, and workgroups run on XCD w mod 8, where the odd-numbered XCDs were measured to
+// stream more slowly.  Workgroup w starts at unit floor(total * c(w) / c(W)), c(w) = the sum
+// of the weights of workgroups 0 .. w-1.
 __device__ __forceinline__ int64_t split_c(const DecodeParams& p, int64_t w) {
+  auto part = [&](int64_t n0, int64_t n1, int tier) {     // weights of workgroups [n0, n1)
+    const int64_t evens = (n1 + 1) / 2 - (n0 + 1) / 2, odds = n1 / 2 - n0 / 2;
+    return evens * p.split_w[2 * tier] + odds * p.split_w[2 * tier + 1];
+  };
   const int64_t h = p.split_tier;
-  return w <= h ? p.split_a * w : p.split_a * h + 16 * (w - h);
+  return w <= h ? part(0, w, 0) : part(0, h, 0) + part(h, w, 1);
 }
 __device__ __forceinline__ int64_t range_start(const DecodeParams& p, int64_t total, int64_t w) {
   return total * split_c(p, w) / split_c(p, p.num_wgs);

@@ -45,7 +45,7 @@ struct DecodeParams {
   int seg_start_units;                // units without tokens ahead of each non-empty segment
   int64_t num_wgs;                    // workgroups in the decode grid
   int64_t split_tier;                 // workgroups of the first dispatch tier (one per CU)
-  int64_t split_a;                    // their share of the units relative to the rest, in 1/16
+  int64_t split_w[4];                 // units share of workgroup w: [tier * 2 + (w & 1)]
   int heads_per_group;                // kv heads one workgroup covers
   int num_head_groups;                // num_kv_heads / heads_per_group
   int token_streams;                  // waves sets of a workgroup splitting its chunks
