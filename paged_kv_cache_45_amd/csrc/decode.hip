@@ -139,7 +139,8 @@ DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int head_di
   int hw = 1;                                    // head waves per workgroup (at most 4)
   for (int w = std::min(waves, 4); w >= 1; --w)
     if (waves % w == 0) { hw = w; break; }
-  P.token_streams = (2 * hw <= kMaxWaves) ? 2 : 1;
+  // token streams: up to 4, within kMaxWaves waves (their chunks are shared out at run time)
+  P.token_streams = std::max(1, std::min(4, kMaxWaves / hw));
   P.waves_per_wg = hw * P.token_streams;
   P.heads_per_group = P.hpi * hw;
   {

@@ -21,11 +21,14 @@
 //    lane owning 8 consecutive elements (one 16-byte load of K and one of V).
 //  * Work (stream-K): requests are cut into granules of `partition_size` tokens; the
 //    (request, head group, granule) units are laid end to end and the grid holds as many
-//    workgroups as the chip keeps resident, each taking an equal contiguous range of
-//    units.  All workgroups stream for the same time, with no tail.  A (request, head
-//    group) segment covered by one workgroup is finished in registers; where a range starts
-//    or ends inside a segment the partial state (m, l, acc) goes to the workspace and a
-//    small second kernel merges it by log-sum-exp.
+//    workgroups as the chip keeps resident, each taking a contiguous range of units sized
+//    to its expected speed, so that all workgroups stream for about the same time.  A
+//    (request, head group) segment covered by one workgroup is finished in registers; where
+//    a range starts or ends inside a segment the partial state (m, l, acc) goes to the
+//    workspace and a small second kernel merges it by log-sum-exp.  Inside a workgroup the
+//    waves are head waves (HPI heads each) times token streams (up to 4): the token streams
+//    of a head wave share its chunks out through an LDS counter and merge their states
+//    through LDS at the end of each segment.
 //  * QK: v_dot2_f32_{bf16,f16} on packed pairs and a DPP reduction inside the lane row;
 //    each row keeps its own online-softmax state (m, l in log2 units, the lane's 8
 //    accumulator columns per query head).
@@ -312,16 +315,23 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
   }
 }
 
-// Reduce the chunks k = stream, stream + TS, ... of tokens [t0, t1) of request b, head group hg
-// into S (this lane's row: head hh of the group, token offset tr inside a wave instruction).
+// Reduce the chunks of tokens [t0, t1) of request b, head group hg into S (this lane's row:
+// head hh of the group, token offset tr inside a wave instruction).  The token streams of one
+// head wave take the chunks from a counter in LDS (`cnt`, zero at the start) rather than a
+// fixed interleave, so that a wave that streams faster (the SIMD issues the oldest waves
+// first) takes more chunks and the workgroup's waves finish the range together.  Physical
+// block ids of up to 64 chunks are fetched with one vector load (lane k <-> k-th chunk of the
+// window) and read back with v_readlane; the next chunk's K/V loads are issued before the
+// current chunk is computed (two register buffers).
 template <int D, int G, bool BF16, CacheKind KIND, int HPI>
 __device__ __forceinline__ void run_range(const DecodeParams& p, State<G>& S, int b, int hg, int t0,
-                                          int t1, int lane, int tr, int hh, int c, int stream) {
+                                                 int t1, int lane, int tr, int hh, int c, int* cnt) {
   using Gm = Geo<D, HPI, G>;
   using R = Regs<Gm::NI, KIND>;
   constexpr int esz = KIND == CacheKind::U3 ? 4 : 2;
   const int nk = (t1 - t0 + Gm::CT - 1) / Gm::CT;
   const bool ragged = ((t1 - t0) % Gm::CT) != 0;
+  const int n_plain = ragged ? nk - 1 : nk;
   const int32_t* bt_row = p.block_tables + b * p.bt_sb;
   const int h_first = hg * p.heads_per_group;
   const LaneOffsets<D, HPI, KIND, G> lo = lane_offsets<D, HPI, KIND, G>(p, tr, hh, c);
@@ -329,49 +339,56 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, State<G>& S, in
   const char* vc = static_cast<const char*>(p.v_cache) + (int64_t)h_first * p.c_sh * esz;
   const char* kmc = static_cast<const char*>(p.k_meta) + (int64_t)h_first * 4;
   const char* vmc = static_cast<const char*>(p.v_meta) + (int64_t)h_first * 4;
-  for (int win = 0; win < nk; win += 64) {
-    const int n = min(64, nk - win);
-    int bt_lane = 0;
-    if (lane < n) {
-      const int e = bt_row[(t0 + (win + lane) * Gm::CT) >> p.log2_bs];
-      bt_lane = (int)min<int64_t>(max(e, 0), p.num_blocks - 1);   // out-of-range ids clamped
-    }
-    auto issue = [&](int k, R& regs) {
-      const int tok0 = t0 + (win + k) * Gm::CT;
-      const int64_t phys = __builtin_amdgcn_readlane(bt_lane, k);
-      const int64_t slot0 = tok0 & (p.block_size - 1);
-      const int64_t rowb = (phys * p.c_sb + slot0 * p.c_ss) * esz;
-      const int64_t metab = ((phys * p.block_size + slot0) * p.num_kv_heads) * 4;
-      load_chunk<D, HPI, KIND, G>(kc + rowb, vc + rowb, kmc + metab, vmc + metab, lo, c, regs);
-    };
-    auto tok_of = [&](int k) { return t0 + (win + k) * Gm::CT + tr; };
-    // this stream's chunks k = first, first + ts, ... of the window; the ragged last chunk of
-    // the range is peeled off so that the loop body holds only the unmasked code, and the
-    // next chunk's loads are always in flight while the current one is computed
-    const int ts = p.token_streams;
-    const int n_plain = (ragged && win + n == nk) ? n - 1 : n;
-    int k = (stream - win % ts + ts) % ts;
-    if (k < n_plain) {
-      R ra, rb;
-      issue(k, ra);
-      for (;;) {
-        const int k1 = k + ts;
-        if (k1 < n_plain) issue(k1, rb);
-        compute_chunk<D, G, BF16, KIND, HPI, false>(p, S, ra, tok_of(k), t1, c);
-        k = k1;
-        if (k >= n_plain) break;
-        const int k2 = k + ts;
-        if (k2 < n_plain) issue(k2, ra);
-        compute_chunk<D, G, BF16, KIND, HPI, false>(p, S, rb, tok_of(k), t1, c);
-        k = k2;
-        if (k >= n_plain) break;
+  typedef __attribute__((address_space(3))) int LdsInt;
+  LdsInt* const cnt_lds = (LdsInt*)cnt;                   // an LDS atomic (ds_add_rtn, lgkmcnt)
+  auto claim = [&]() {
+    int v = 0;
+    if (lane == 0) v = __hip_atomic_fetch_add(cnt_lds, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  // physical block ids of chunks [win, win + 64), lane k <-> chunk win + k; claims only grow,
+  // so the window only moves forward
+  int win = 0, bt_lane = 0;
+  bool have = false;
+  auto issue = [&](int k, R& regs) {
+    if (!have || k - win >= 64) {
+      win = k;
+      have = true;
+      bt_lane = 0;
+      if (win + lane < nk) {
+        const int e = bt_row[(t0 + (win + lane) * Gm::CT) >> p.log2_bs];
+        bt_lane = (int)min<int64_t>(max(e, 0), p.num_blocks - 1);   // out-of-range ids clamped
       }
     }
-    if (n_plain < n && k == n - 1) {
-      R regs;
-      issue(n - 1, regs);
-      compute_chunk<D, G, BF16, KIND, HPI, true>(p, S, regs, tok_of(n - 1), t1, c);
+    const int tok0 = t0 + k * Gm::CT;
+    const int64_t phys = __builtin_amdgcn_readlane(bt_lane, k - win);
+    const int64_t slot0 = tok0 & (p.block_size - 1);
+    const int64_t rowb = (phys * p.c_sb + slot0 * p.c_ss) * esz;
+    const int64_t metab = ((phys * p.block_size + slot0) * p.num_kv_heads) * 4;
+    load_chunk<D, HPI, KIND, G>(kc + rowb, vc + rowb, kmc + metab, vmc + metab, lo, c, regs);
+  };
+  auto tok_of = [&](int k) { return t0 + k * Gm::CT + tr; };
+  int k = claim();
+  if (k < n_plain) {
+    R ra, rb;
+    issue(k, ra);
+    for (;;) {
+      const int k1 = claim();
+      if (k1 < n_plain) issue(k1, rb);
+      compute_chunk<D, G, BF16, KIND, HPI, false>(p, S, ra, tok_of(k), t1, c);
+      k = k1;
+      if (k >= n_plain) break;
+      const int k2 = claim();
+      if (k2 < n_plain) issue(k2, ra);
+      compute_chunk<D, G, BF16, KIND, HPI, false>(p, S, rb, tok_of(k), t1, c);
+      k = k2;
+      if (k >= n_plain) break;
     }
+  }
+  if (ragged && k == n_plain) {          // the ragged last chunk, taken by exactly one wave
+    R regs;
+    issue(k, regs);
+    compute_chunk<D, G, BF16, KIND, HPI, true>(p, S, regs, tok_of(k), t1, c);
   }
 }
 
@@ -403,9 +420,11 @@ __device__ __forceinline__ void run_claimed(const DecodeParams& p, State<G>& S, 
   // a claim outside [0, nu) ends the loop: a counter that is not zero at the start of the call
   // (a workspace that was not zero-filled) can only lose work, never read outside the segment
   auto take = [&](int v) { return (unsigned)v < (unsigned)nu ? v : nu; };
+  typedef __attribute__((address_space(1))) int GlobalInt;
+  GlobalInt* const claim_g = (GlobalInt*)claim;          // a global atomic (vmcnt only)
   auto claim_async = [&]() {
     int v = 0;
-    if (lane == 0) v = atomicAdd(claim, 1);
+    if (lane == 0) v = __hip_atomic_fetch_add(claim_g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return v;
   };
   // unit u's block (id through the scalar cache) and first slot in it
@@ -526,7 +545,11 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
   using Gm = Geo<D, HPI, G>;
   extern __shared__ int s_pref[];              // batch + 1 entries
   __shared__ int s_tile[kMaxWaves];
-  build_prefix(p, s_pref, s_tile);
+  // chunk counters of the head waves' token streams, one set per segment parity: the set of
+  // segment i + 1 is cleared during segment i, after the barriers that end segment i - 1
+  __shared__ int s_cnt[2][kMaxWaves];
+  if (threadIdx.x < 2 * kMaxWaves) s_cnt[threadIdx.x / kMaxWaves][threadIdx.x % kMaxWaves] = 0;
+  build_prefix(p, s_pref, s_tile);             // (ends with a barrier)
 
   const int lane = threadIdx.x & 63;
   const int hw_count = p.heads_per_group / HPI;  // waves per token stream
@@ -552,6 +575,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
     return;
   }
   bool first = true;
+  int seg_i = 0;
   while (x < x_end) {
     // segment (request b, head group hg) holding unit x: the last b with NHG*s_pref[b] <= x
     int lo = 0, hi = p.batch;
@@ -595,6 +619,11 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
 #pragma unroll
       for (int e = 0; e < 8; ++e) PKV_ACC(S, g, e) = 0.f;
     }
+    if (seg_i > 0 && threadIdx.x < kMaxWaves) s_cnt[(seg_i + 1) & 1][threadIdx.x] = 0;
+    int* cnt = &s_cnt[seg_i & 1][wv];
+    auto range = [&](int ta, int tb) {
+      run_range<D, G, BF16, KIND, HPI>(p, S, b, hg, ta, tb, lane, tr, hh, c, cnt);
+    };
     if constexpr (CLAIM) {
       if (!(g0 == 0 && g1 == n)) {
         // a shared segment: its full claim units by claim; the ragged tail (if any) by the
@@ -603,13 +632,12 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
         run_claimed<D, G, BF16, KIND, HPI>(p, S, b, hg, nu,
                                            p.ws_claim + ((int64_t)b * NHG + hg) * kClaimWaves + wv,
                                            lane, tr, hh, c, stream);
-        if (g1 == n && (nu << p.log2_claim) < ctx)
-          run_range<D, G, BF16, KIND, HPI>(p, S, b, hg, nu << p.log2_claim, ctx, lane, tr, hh, c, stream);
+        if (g1 == n && (nu << p.log2_claim) < ctx) range(nu << p.log2_claim, ctx);
       } else {
-        run_range<D, G, BF16, KIND, HPI>(p, S, b, hg, t0, t1, lane, tr, hh, c, stream);
+        range(t0, t1);
       }
     } else {
-      run_range<D, G, BF16, KIND, HPI>(p, S, b, hg, t0, t1, lane, tr, hh, c, stream);
+      range(t0, t1);
     }
     merge_rows<D, G, KIND, HPI>(S);
     if (p.token_streams > 1) {
@@ -666,6 +694,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
     }
     x += g1 - g0;
     first = false;
+    ++seg_i;
   }
 }
 

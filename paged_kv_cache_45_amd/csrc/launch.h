@@ -64,7 +64,7 @@ struct DecodePlan {
   int waves_per_wg;
   int heads_per_group;                // hpi * (waves_per_wg / token_streams)
   int num_head_groups;
-  int token_streams;                  // interleaved chunk streams per workgroup
+  int token_streams;                  // waves per head wave sharing out its chunks
   int64_t num_wgs;                    // as many as stay resident, at most one per unit
   int64_t split_tier;                 // first dispatch tier: min(num_wgs, compute units)
   int chunk_tokens;                   // tokens per chunk of a token stream
