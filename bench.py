@@ -43,7 +43,7 @@ N_LAYERS = 4
 METRIC = "paged decode KV GB/s (% of HBM peak) + append tokens/s, Llama-8B shape"
 DECODE_SOURCES = ("paged_kv_cache_45_amd/csrc/decode.hip", "paged_kv_cache_45_amd/csrc/decode_kernel.cuh",
                   "paged_kv_cache_45_amd/csrc/decode_same_d128.hip", "paged_kv_cache_45_amd/csrc/common.cuh",
-                  "paged_kv_cache_45_amd/csrc/launch.h")
+                  "paged_kv_cache_45_amd/csrc/launch.h", "paged_kv_cache_45_amd/csrc/api.cpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama8b_hbm_traffic.md")
 
 
