@@ -42,6 +42,7 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 template <bool BF16>
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   if constexpr (BF16) {

@@ -218,31 +218,40 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
       for (int g = 0; g < G; ++g) sc[i][g] = valid[i] ? d[g] * p.scale_log2 : neg_inf();
     }
   } else {
-    const int sh = (24 * c) & 31;
+    // The lane's octet starts at byte (3c) mod 4 of (klo, khi); one byte permute gives
+    // y = [bits 0..15 | bits 8..23] of the octet, so that code e sits at bit 3e of the low half
+    // and code e + 4 at bit 3e + 4 of the high half, and one packed 16-bit shift per pair
+    // lines up (code e, code e + 4) for the dot product with (q[e], q[e + 4]).
+    const uint32_t sel = (uint32_t)((3 * c) & 3) * 0x01010101u + 0x02010100u;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const uint32_t ko = __builtin_amdgcn_alignbit(R.khi[i], R.klo[i], sh) & 0xffffffu;
+      const uint32_t y = __builtin_amdgcn_perm(R.khi[i], R.klo[i], sel);
       // codes as packed 16-bit pairs: fp16 exactly (1024 + c, minus 1024); bf16 pairs keep a
       // +128 offset that is folded into the zero point below
       uint32_t cp[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t a = (ko >> (6 * e)) & 7u, bb = (ko >> (6 * e + 3)) & 7u;
+        const u16x2_t sh2 = {(uint16_t)(3 * e), (uint16_t)(3 * e + 4)};
+        const uint32_t pr = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2_t, y) >> sh2) & 0x00070007u;
         if constexpr (BF16) {
-          cp[e] = (a | (bb << 16)) | 0x43004300u;
+          cp[e] = pr | 0x43004300u;
         } else {
-          const uint32_t magic = (a | (bb << 16)) | 0x64006400u;
-          const f16x2_t v = __builtin_bit_cast(f16x2_t, magic) - (f16x2_t){1024.0f16, 1024.0f16};
+          const f16x2_t v = __builtin_bit_cast(f16x2_t, pr | 0x64006400u) - (f16x2_t){1024.0f16, 1024.0f16};
           cp[e] = __builtin_bit_cast(uint32_t, v);
         }
       }
-      float d[G];                      // (one value at a time: the stage-major schedule spills)
+      float d[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         d[g] = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) d[g] = dot2<BF16>(S.qv[g][e], cp[e], d[g]);
-        d[g] = group_sum<LPR>(d[g]);
+      }
+      if constexpr (G <= 4) {
+        group_sum_n<LPR>(d);
+      } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g) d[g] = group_sum<LPR>(d[g]);
       }
       const float ks = f16_lo(R.km[i]), kz = f16_hi(R.km[i]);
       const float off = BF16 ? 128.f + kz : kz;
@@ -301,10 +310,10 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
       }
       pv_accumulate<G>(S, pp[i], 1.f, vf);
     } else {
-      const int sh = (24 * c) & 31;
-      const uint32_t vo = __builtin_amdgcn_alignbit(R.vhi[i], R.vlo[i], sh) & 0xffffffu;
+      // the same byte permute: codes 0..4 at bits 3e, codes 5..7 at bits 3e + 8
+      const uint32_t y = __builtin_amdgcn_perm(R.vhi[i], R.vlo[i], (uint32_t)((3 * c) & 3) * 0x01010101u + 0x02010100u);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vf[e] = (float)((vo >> (3 * e)) & 7u);
+      for (int e = 0; e < 8; ++e) vf[e] = (float)((y >> (e < 5 ? 3 * e : 3 * e + 8)) & 7u);
       const float vs = valid[i] ? f16_lo(R.vm[i]) : 0.f;
       const float vz = valid[i] ? f16_hi(R.vm[i]) : 0.f;
       // sum_t p (code - z) s = sum_t (p s) code - sum_t (p s) z
@@ -605,7 +614,15 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
     for (int g = 0; g < G; ++g) {
       const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) +
                                                       b * p.q_sb + (int64_t)(h * G + g) * p.q_sh + c * 8);
-      S.qv[g][0] = v.x; S.qv[g][1] = v.y; S.qv[g][2] = v.z; S.qv[g][3] = v.w;
+      if constexpr (KIND == CacheKind::U3) {
+        // pairs (q[e], q[e + 4]) of the lane's 8 elements, the order the 3-bit codes unpack in
+        S.qv[g][0] = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
+        S.qv[g][1] = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
+        S.qv[g][2] = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
+        S.qv[g][3] = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
+      } else {
+        S.qv[g][0] = v.x; S.qv[g][1] = v.y; S.qv[g][2] = v.z; S.qv[g][3] = v.w;
+      }
       S.qsum[g] = 0.f;
       if constexpr (KIND == CacheKind::U3) {
         float s = 0.f;
