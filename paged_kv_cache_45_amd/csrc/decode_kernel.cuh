@@ -108,16 +108,22 @@ struct State {
 // itself, register m of lane (row, c) gains w * p[m] * v[e], the same as the FMA form.
 // With G = 8 the extra operand registers push the kernel into spills (measured 7 % slower on
 // the long-context decode), so G = 8 keeps the FMA form.
+constexpr int kMfmaMaxG = 4;
+
 template <int G, typename St>
 __device__ __forceinline__ void pv_accumulate(St& S, const float (&p)[G], float w, const float (&v)[8]) {
-  if constexpr (G <= 4) {
+  if constexpr (G <= kMfmaMaxG) {
     const int q = threadIdx.x & 3;
-    float a = 0.f;                                  // heads g >= G of the quad stay 0
 #pragma unroll
-    for (int m = 0; m < G; ++m) a = (q == m) ? p[m] : a;
-    a *= w;
+    for (int h4 = 0; h4 < (G + 3) / 4; ++h4) {      // query heads 4 h4 .. 4 h4 + 3
+      float a = 0.f;                                // heads g >= G of the quad stay 0
 #pragma unroll
-    for (int e = 0; e < 8; ++e) S.acc4[0][e] = __builtin_amdgcn_mfma_f32_4x4x1f32(a, v[e], S.acc4[0][e], 0, 0, 0);
+      for (int m = 0; m < 4 && 4 * h4 + m < G; ++m) a = (q == m) ? p[4 * h4 + m] : a;
+      a *= w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        S.acc4[h4][e] = __builtin_amdgcn_mfma_f32_4x4x1f32(a, v[e], S.acc4[h4][e], 0, 0, 0);
+    }
   } else {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
