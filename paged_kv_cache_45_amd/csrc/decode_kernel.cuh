@@ -170,8 +170,8 @@ __device__ __forceinline__ void load_chunk(const char* kb, const char* vb, const
   if constexpr (KIND == CacheKind::Same) {
 #pragma unroll
     for (int i = 0; i < Gm::NI; ++i) {
-      R.k[i] = *reinterpret_cast<const uint4*>(kb + o.row[i]);
-      R.v[i] = *reinterpret_cast<const uint4*>(vb + o.row[i]);
+      R.k[i] = load_stream_u4(kb + o.row[i]);
+      R.v[i] = load_stream_u4(vb + o.row[i]);
     }
   } else {
     // 3-bit rows: D*3/32 words; lane c owns octet c = stream bits [24c, 24c + 24), which
@@ -179,12 +179,12 @@ __device__ __forceinline__ void load_chunk(const char* kb, const char* vb, const
     const bool two = ((c & 3) == 1) || ((c & 3) == 2);
 #pragma unroll
     for (int i = 0; i < Gm::NI; ++i) {
-      R.klo[i] = *reinterpret_cast<const uint32_t*>(kb + o.row[i]);
-      R.khi[i] = two ? *reinterpret_cast<const uint32_t*>(kb + o.row[i] + 4) : 0u;
-      R.vlo[i] = *reinterpret_cast<const uint32_t*>(vb + o.row[i]);
-      R.vhi[i] = two ? *reinterpret_cast<const uint32_t*>(vb + o.row[i] + 4) : 0u;
-      R.km[i] = *reinterpret_cast<const uint32_t*>(kmb + o.meta[i]);
-      R.vm[i] = *reinterpret_cast<const uint32_t*>(vmb + o.meta[i]);
+      R.klo[i] = load_stream_u32(kb + o.row[i]);
+      R.khi[i] = two ? load_stream_u32(kb + o.row[i] + 4) : 0u;
+      R.vlo[i] = load_stream_u32(vb + o.row[i]);
+      R.vhi[i] = two ? load_stream_u32(vb + o.row[i] + 4) : 0u;
+      R.km[i] = load_stream_u32(kmb + o.meta[i]);
+      R.vm[i] = load_stream_u32(vmb + o.meta[i]);
     }
   }
 }
