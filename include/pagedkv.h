@@ -127,14 +127,18 @@ size_t paged_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads,
  * context_lens[b] tokens, token t read from physical block block_tables[b, t /
  * block_size] at slot t % block_size; GQA per [Append] (query head h reads kv head
  * h / (num_q_heads / num_kv_heads)); with the 3-bit cache the codes are unpacked and
- * dequantised, x = (q - z) * s, on the fly ([3bit], title paragraph, section 2 test 3).
+ * dequantised, x = (q - z) * s, on the fly ([3bit], title paragraph, section 2 test 3);
+ * with the fp8 cache each row reads as decode_e4m3fn(code) * s, the inverse of the
+ * kv_append quantiser ([Append], Correctness requirements: the quantised cache is read back
+ * through the row's scale), with s applied to the row's dot product and to its probability.
  *
  *   out, q           device [batch, num_q_heads, head_dim] of q_dtype (F16 or BF16);
  *                    element (b, h, d) at b*stride_b + h*stride_h + d; out has the
  *                    same dtype.  16-byte aligned rows.
  *   k_cache, v_cache pools as for kv_append; cache_dtype == q_dtype, or PKV_U3 (with
- *                    k_meta, v_meta fp16 (s, z) as for kv_append).  PKV_FP8_E4M3FN
- *                    decode is not provided (PKV_EUNSUPPORTED).
+ *                    k_meta, v_meta fp16 (s, z) as for kv_append), or PKV_FP8_E4M3FN (with
+ *                    k_meta, v_meta fp32 per-row scales as for kv_append; pools 8-byte
+ *                    aligned, strides multiples of 8, else PKV_EINVAL).
  *   block_tables     device int32 [batch, bt_stride_b >= cdiv(max_context_len,
  *                    block_size)]; entries at or beyond cdiv(context_lens[b],
  *                    block_size) are never read.  Entries must be < num_blocks.

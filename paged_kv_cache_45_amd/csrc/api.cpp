@@ -216,7 +216,6 @@ int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
   if (!known(q_dtype) || !known(cache_dtype)) return PKV_EINVAL;
   if (!is16(q_dtype)) return PKV_EUNSUPPORTED;
   if (is16(cache_dtype) && cache_dtype != q_dtype) return PKV_EINVAL;
-  if (cache_dtype == PKV_FP8_E4M3FN) return PKV_EUNSUPPORTED;
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_context_len < 0)
     return PKV_EINVAL;
   if (batch > kMaxBatch) return PKV_EUNSUPPORTED;
@@ -242,6 +241,13 @@ int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
     kind = CacheKind::U3;
     if (!aligned(k_cache, 4) || !aligned(v_cache, 4)) return PKV_EINVAL;
     if (!k_meta || !v_meta || !aligned(k_meta, 4) || !aligned(v_meta, 4)) return PKV_EINVAL;
+  } else if (cache_dtype == PKV_FP8_E4M3FN) {
+    // one lane reads 8 codes (8 bytes) of a row; one fp32 scale per (slot, kv head)
+    kind = CacheKind::Fp8;
+    if (!aligned(k_cache, 8) || !aligned(v_cache, 8) || c_stride_block % 8 || c_stride_slot % 8 ||
+        c_stride_head % 8)
+      return PKV_EINVAL;
+    if (!k_meta || !v_meta || !aligned(k_meta, 4) || !aligned(v_meta, 4)) return PKV_EINVAL;
   } else {
     if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || c_stride_block % 8 ||
         c_stride_slot % 8 || c_stride_head % 8)
@@ -257,7 +263,7 @@ int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
   if ((int64_t)batch * num_kv_heads * cdiv(max_context_len, ps) > 0x7fffffffLL) return PKV_EUNSUPPORTED;
   if (batch == 0) return PKV_OK;
   const DecodeLayout L = decode_layout(batch, num_q_heads, num_kv_heads, head_dim, max_context_len, ps,
-                                       q_dtype == PKV_BF16 ? 1 : 0, kind == CacheKind::U3 ? 1 : 0);
+                                       q_dtype == PKV_BF16 ? 1 : 0, static_cast<int>(kind));
   if (!workspace || workspace_bytes < L.bytes || !aligned(workspace, 256)) return PKV_EWORKSPACE;
 
   pkv::DecodeParams p{};
@@ -303,7 +309,9 @@ int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
   // granules leave a tail (measured: 128 KB blocks of the long-context decode gain ~10 %, 32 KB
   // blocks of the Llama-8B step lose 15 %): at least 64 KB of K/V per wave and block.  It also
   // needs an even number of chunks per block and at most 4 head waves.
-  const int64_t row_bytes = cache_dtype == PKV_U3 ? 2 * (head_dim * 3 / 8 + 4) : 4 * (int64_t)head_dim;
+  const int64_t row_bytes = cache_dtype == PKV_U3    ? 2 * (head_dim * 3 / 8 + 4)
+                            : cache_dtype == PKV_FP8_E4M3FN ? 2 * (int64_t)(head_dim + 4)
+                                                            : 4 * (int64_t)head_dim;
   const int64_t wave_block_bytes = (int64_t)block_size * L.plan.hpi * row_bytes;
   const int unit_tokens = kClaimUnitChunks > 0 ? std::min(block_size, kClaimUnitChunks * L.plan.chunk_tokens)
                                                : block_size;

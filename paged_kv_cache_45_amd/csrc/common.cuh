@@ -54,6 +54,11 @@ __device__ __forceinline__ uint4 load_stream_u4(const void* p) {
   const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+__device__ __forceinline__ uint2 load_stream_u2(const void* p) {
+  typedef uint32_t u32x2_nt __attribute__((ext_vector_type(2)));
+  const u32x2_nt v = __builtin_nontemporal_load(static_cast<const u32x2_nt*>(p));
+  return make_uint2(v.x, v.y);
+}
 __device__ __forceinline__ uint32_t load_stream_u32(const void* p) {
   return __builtin_nontemporal_load(static_cast<const uint32_t*>(p));
 }

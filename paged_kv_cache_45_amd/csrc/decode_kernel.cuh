@@ -41,6 +41,7 @@
 
 #include "launch.h"
 #include "common.cuh"
+#include "fp8_quant.cuh"
 
 namespace pkv {
 
@@ -84,6 +85,10 @@ struct Geo {
 
 template <int NI, CacheKind KIND> struct Regs;
 template <int NI> struct Regs<NI, CacheKind::Same> { uint4 k[NI], v[NI]; };
+template <int NI> struct Regs<NI, CacheKind::Fp8> {
+  uint2 k[NI], v[NI];                // 8 e4m3fn codes of the lane's row
+  float ks[NI], vs[NI];              // the row's scales
+};
 template <int NI> struct Regs<NI, CacheKind::U3> {
   uint32_t klo[NI], khi[NI], vlo[NI], vhi[NI], km[NI], vm[NI];
 };
@@ -149,7 +154,7 @@ __device__ __forceinline__ LaneOffsets<D, HPI, KIND, G> lane_offsets(const Decod
                                                                    int c) {
   using Gm = Geo<D, HPI, G>;
   LaneOffsets<D, HPI, KIND, G> o;
-  constexpr int esz = KIND == CacheKind::U3 ? 4 : 2;
+  constexpr int esz = KIND == CacheKind::U3 ? 4 : KIND == CacheKind::Fp8 ? 1 : 2;
   const int col = KIND == CacheKind::U3 ? ((3 * c) >> 2) : c * 8;
 #pragma unroll
   for (int i = 0; i < Gm::NI; ++i) {
@@ -172,6 +177,14 @@ __device__ __forceinline__ void load_chunk(const char* kb, const char* vb, const
     for (int i = 0; i < Gm::NI; ++i) {
       R.k[i] = load_stream_u4(kb + o.row[i]);
       R.v[i] = load_stream_u4(vb + o.row[i]);
+    }
+  } else if constexpr (KIND == CacheKind::Fp8) {
+#pragma unroll
+    for (int i = 0; i < Gm::NI; ++i) {
+      R.k[i] = load_stream_u2(kb + o.row[i]);
+      R.v[i] = load_stream_u2(vb + o.row[i]);
+      R.ks[i] = *reinterpret_cast<const float*>(kmb + o.meta[i]);
+      R.vs[i] = *reinterpret_cast<const float*>(vmb + o.meta[i]);
     }
   } else {
     // 3-bit rows: D*3/32 words; lane c owns octet c = stream bits [24c, 24c + 24), which
@@ -201,10 +214,20 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
 #pragma unroll
   for (int i = 0; i < NI; ++i) valid[i] = !MASKED || (tok + i * Gm::TPI < t_end);
   float sc[NI][G];
-  if constexpr (KIND == CacheKind::Same) {
+  if constexpr (KIND == CacheKind::Same || KIND == CacheKind::Fp8) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const uint32_t kw[4] = {R.k[i].x, R.k[i].y, R.k[i].z, R.k[i].w};
+      uint32_t kw[4];
+      if constexpr (KIND == CacheKind::Same) {
+        kw[0] = R.k[i].x; kw[1] = R.k[i].y; kw[2] = R.k[i].z; kw[3] = R.k[i].w;
+      } else {
+        // fp8: the 8 codes as exact 16-bit pairs of the query's type; the row scale multiplies
+        // the dot product: (s k) . q = s (k . q)
+        kw[0] = fp8x2_to_16<BF16, false>(R.k[i].x);
+        kw[1] = fp8x2_to_16<BF16, true>(R.k[i].x);
+        kw[2] = fp8x2_to_16<BF16, false>(R.k[i].y);
+        kw[3] = fp8x2_to_16<BF16, true>(R.k[i].y);
+      }
       float d[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -220,8 +243,10 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
 #pragma unroll
         for (int g = 0; g < G; ++g) d[g] = group_sum<LPR>(d[g]);
       }
+      float scl = p.scale_log2;
+      if constexpr (KIND == CacheKind::Fp8) scl *= R.ks[i];
 #pragma unroll
-      for (int g = 0; g < G; ++g) sc[i][g] = valid[i] ? d[g] * p.scale_log2 : neg_inf();
+      for (int g = 0; g < G; ++g) sc[i][g] = valid[i] ? d[g] * scl : neg_inf();
     }
   } else {
     // The lane's octet starts at byte (3c) mod 4 of (klo, khi); one byte permute gives
@@ -315,6 +340,16 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
         vf[2 * e + 1] = h_hi<BF16>(vw[e]);
       }
       pv_accumulate<G>(S, pp[i], 1.f, vf);
+    } else if constexpr (KIND == CacheKind::Fp8) {
+      uint32_t vw0 = R.v[i].x, vw1 = R.v[i].y;
+      float vs = R.vs[i];
+      if (MASKED && !valid[i]) { vw0 = vw1 = 0u; vs = 0.f; }          // poisoned tails stay out
+      fp8x2_to_f32<false>(vw0, vf[0], vf[1]);
+      fp8x2_to_f32<true>(vw0, vf[2], vf[3]);
+      fp8x2_to_f32<false>(vw1, vf[4], vf[5]);
+      fp8x2_to_f32<true>(vw1, vf[6], vf[7]);
+      // sum_t p (s v_t) = sum_t (p s) v_t
+      pv_accumulate<G>(S, pp[i], vs, vf);
     } else {
       // the same byte permute: codes 0..4 at bits 3e, codes 5..7 at bits 3e + 8
       const uint32_t y = __builtin_amdgcn_perm(R.vhi[i], R.vlo[i], (uint32_t)((3 * c) & 3) * 0x01010101u + 0x02010100u);
@@ -343,7 +378,7 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, State<G>& S, in
                                                  int t1, int lane, int tr, int hh, int c, int* cnt) {
   using Gm = Geo<D, HPI, G>;
   using R = Regs<Gm::NI, KIND>;
-  constexpr int esz = KIND == CacheKind::U3 ? 4 : 2;
+  constexpr int esz = KIND == CacheKind::U3 ? 4 : KIND == CacheKind::Fp8 ? 1 : 2;
   const int nk = (t1 - t0 + Gm::CT - 1) / Gm::CT;
   const bool ragged = ((t1 - t0) % Gm::CT) != 0;
   const int n_plain = ragged ? nk - 1 : nk;
@@ -422,7 +457,7 @@ __device__ __forceinline__ void run_claimed(const DecodeParams& p, State<G>& S, 
                                             int* claim, int lane, int tr, int hh, int c, int stream) {
   using Gm = Geo<D, HPI, G>;
   using R = Regs<Gm::NI, KIND>;
-  constexpr int esz = KIND == CacheKind::U3 ? 4 : 2;
+  constexpr int esz = KIND == CacheKind::U3 ? 4 : KIND == CacheKind::Fp8 ? 1 : 2;
   const int my_n = (1 << p.log2_claim) / Gm::CT;          // chunks per unit
   typedef const __attribute__((address_space(4))) int32_t* ConstIntPtr;
   const ConstIntPtr bt_row = (ConstIntPtr)(p.block_tables + b * p.bt_sb);
@@ -722,9 +757,9 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
 }
 
 // ---------------------------------------------------------------------------------------
-// Instance lookup.  The instances are compiled in four translation units (decode_same_d128,
-// decode_same_d64, decode_u3_d128, decode_u3_d64), each exporting the pointer lookup of its
-// head dim and cache kind, so that the build can compile them in parallel.
+// Instance lookup.  The instances are compiled in six translation units (decode_{same, fp8,
+// u3}_d{128, 64}), each exporting the pointer lookup of its head dim and cache kind, so that
+// the build can compile them in parallel.
 // ---------------------------------------------------------------------------------------
 template <int D, int G, bool BF16, CacheKind KIND, int HPI>
 const void* kernel_ptr(bool claim) {
@@ -762,6 +797,8 @@ const void* kernel_by_dtype(int group, bool bf16, int hpi, bool claim) {
 // host pointer of decode_kernel<D, group, bf16, KIND, hpi, claim>, or nullptr if not built
 const void* decode_kernel_ptr_same_d128(int group, bool bf16, int hpi, bool claim);
 const void* decode_kernel_ptr_same_d64(int group, bool bf16, int hpi, bool claim);
+const void* decode_kernel_ptr_fp8_d128(int group, bool bf16, int hpi, bool claim);
+const void* decode_kernel_ptr_fp8_d64(int group, bool bf16, int hpi, bool claim);
 const void* decode_kernel_ptr_u3_d128(int group, bool bf16, int hpi, bool claim);
 const void* decode_kernel_ptr_u3_d64(int group, bool bf16, int hpi, bool claim);
 

@@ -1,4 +1,5 @@
-// fp8 e4m3fn quantisation arithmetic of one cache row.
+// fp8 e4m3fn quantisation arithmetic of one cache row, and the decode's code-to-value
+// conversions.
 //
 // "Write Triton Kv Cache Append Kernel", Required reasoning process step 6 and Failure modes:
 // each value is divided by the row's scale in fp32 before it is cast, and the cast saturates
@@ -55,6 +56,29 @@ __device__ __forceinline__ uint32_t fp8_pack4(float y0, float y1, float y2, floa
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, w, true);
   return (uint32_t)w;
+}
+
+// ---- read side: e4m3fn codes back to values, exactly.  Every e4m3fn value (|v| <= 448,
+// multiples of 2^-9 at the bottom) is exactly a bf16, an fp16 and an fp32 value, so these
+// conversions are exact; the row's scale is applied separately by the caller.
+typedef __bf16 pkv_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 pkv_f16x2_t __attribute__((ext_vector_type(2)));
+
+// codes in bytes 2 HI and 2 HI + 1 of w -> a packed pair of 16-bit values (bf16 or fp16)
+template <bool BF16, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_16(uint32_t w) {
+  if constexpr (BF16) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+  }
+}
+// codes in bytes 2 HI and 2 HI + 1 of w -> two fp32 values
+template <bool HI>
+__device__ __forceinline__ void fp8x2_to_f32(uint32_t w, float& lo, float& hi) {
+  const auto v = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+  lo = v[0];
+  hi = v[1];
 }
 
 }  // namespace pkv

@@ -84,8 +84,8 @@ hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan, CacheKin
 // Split granule used when the caller passes 0.
 int auto_partition_size(int max_context_len, int batch, int num_q_heads);
 
-// Launch geometry on the current device; bf16 / kind = -1 plans for the largest grid any
-// dtype or cache kind would use (for sizing a workspace).
+// Launch geometry on the current device; kind is a CacheKind value.  bf16 / kind = -1 plans
+// for the largest grid any dtype or cache kind would use (for sizing a workspace).
 DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int head_dim, int max_context_len,
                        int partition_size, int bf16, int kind);
 

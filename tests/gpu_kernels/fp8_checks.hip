@@ -1,5 +1,6 @@
-// Test-only kernels: exhaustive checks of the fp8 quantisation shortcuts in
-// paged_kv_cache_45_amd/csrc/fp8_quant.cuh against their plain definitions.  Built next to
+// Test-only kernels: exhaustive checks of the fp8 quantisation shortcuts and the decode's
+// code-to-value conversions in paged_kv_cache_45_amd/csrc/fp8_quant.cuh against their plain
+// definitions.  Built next to
 // this file as libpkv_fp8_checks.so by the package build; loaded only by
 // tests/test_gpu_fp8_exhaustive.py.  Every kernel writes one count (or one code) per thread
 // with a plain store; no atomics.
@@ -65,7 +66,31 @@ __global__ void quotient_codes(int bf16, uint32_t* bad) {
   bad[blockIdx.x * blockDim.x + threadIdx.x] = nbad;
 }
 
+// The decode's code-to-value conversions, for every code c: thread c converts the word
+// c * 0x01010101 with both byte-pair selects.  out16[4c + 0..1] = bf16 pairs (low, high
+// select), out16[4c + 2..3] = fp16 pairs; out32[4c + 0..3] = fp32 values (low pair, high pair).
+__global__ void dequant_codes(uint32_t* out16, float* out32) {
+  const uint32_t c = threadIdx.x;
+  const uint32_t w = c * 0x01010101u;
+  out16[4 * c + 0] = pkv::fp8x2_to_16<true, false>(w);
+  out16[4 * c + 1] = pkv::fp8x2_to_16<true, true>(w);
+  out16[4 * c + 2] = pkv::fp8x2_to_16<false, false>(w);
+  out16[4 * c + 3] = pkv::fp8x2_to_16<false, true>(w);
+  float a, b;
+  pkv::fp8x2_to_f32<false>(w, a, b);
+  out32[4 * c + 0] = a;
+  out32[4 * c + 1] = b;
+  pkv::fp8x2_to_f32<true>(w, a, b);
+  out32[4 * c + 2] = a;
+  out32[4 * c + 3] = b;
+}
+
 }  // namespace
+
+extern "C" int fp8chk_dequant_codes(uint32_t* out16, float* out32, hipStream_t s) {
+  hipLaunchKernelGGL(dequant_codes, dim3(1), dim3(256), 0, s, out16, out32);
+  return (int)hipGetLastError();
+}
 
 extern "C" int fp8chk_hw_codes(uint32_t u0, uint32_t n_threads, uint8_t* codes, uint32_t* bad,
                                hipStream_t s) {

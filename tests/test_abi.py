@@ -81,7 +81,9 @@ def _decode(lib, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(out=None), -1), (dict(bt=None), -1), (dict(Hq=24, Hkv=8), -2), (dict(Hq=30), -1),
-    (dict(Hq=128, Hkv=8), -2), (dict(D=256), -2), (dict(bs=48), -1), (dict(cdt=2), -2),
+    (dict(Hq=128, Hkv=8), -2), (dict(D=256), -2), (dict(bs=48), -1),
+    (dict(cdt=2), -1),                                     # fp8 cache without its scale arrays
+    (dict(cdt=2, km=FAKE, vm=FAKE, cs=1028), -1),          # fp8 rows must stay 8-byte aligned
     (dict(qdt=0), -1), (dict(bts=100), -1), (dict(ps=24), -1), (dict(ps=1 << 21), -2),
     (dict(B=9000, bts=257), -2),
     (dict(ws=None), -3), (dict(wsb=100), -3), (dict(scale=float("nan")), -1),

@@ -6,6 +6,8 @@
 2. The hardware cast v_cvt_pk_fp8_f32 equals the plain integer round-to-nearest-even encoder
    for every fp32 value in [-448, 448], and torch's CPU float8_e4m3fn cast (which the oracle
    is pinned to) for every fp32 value in [0, 448].
+3. The decode's conversions of codes back to bf16, fp16 and fp32 values give the oracle's
+   e4m3fn value of every one of the 254 non-NaN codes, exactly, for both byte-pair selects.
 
 The kernels live in tests/gpu_kernels/fp8_checks.hip and include the library's header, so
 the checked code is the code the append kernel runs.
@@ -32,6 +34,7 @@ def _lib():
     vp = ctypes.c_void_p
     lib.fp8chk_hw_codes.argtypes = [ctypes.c_uint32, ctypes.c_uint32, vp, vp, vp]
     lib.fp8chk_quotient_codes.argtypes = [ctypes.c_int, vp, vp]
+    lib.fp8chk_dequant_codes.argtypes = [vp, vp, vp]
     return lib
 
 
@@ -65,3 +68,28 @@ def test_hardware_cast_matches_rne_and_torch_cpu_cast():
         got = codes[:n].cpu()
         assert torch.equal(got, want), f"hardware cast differs from torch's CPU cast in [{u0:#x}, {u0 + n:#x})"
     assert total_bad == 0, "hardware cast differs from the integer RNE encoder"
+
+
+@pytest.mark.gpu
+def test_decode_conversions_are_exact_for_every_code():
+    from oracle import e4m3fn_decode_table
+    lib = _lib()
+    out16 = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    out32 = torch.zeros(1024, dtype=torch.float32, device="cuda")
+    assert lib.fp8chk_dequant_codes(out16.data_ptr(), out32.data_ptr(),
+                                    torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    w16 = out16.cpu().numpy().view(np.uint32).reshape(256, 4)
+    f32 = out32.cpu().numpy().reshape(256, 4)
+    table = e4m3fn_decode_table()                        # float64 [256], NaN for 0x7F / 0xFF
+    for c in range(256):
+        v = table[c]
+        if np.isnan(v):
+            assert np.all(np.isnan(f32[c]))
+            continue
+        bf = np.uint32(np.float32(v).view(np.uint32) >> 16)
+        hf = np.uint32(np.float16(v).view(np.uint16))
+        assert np.float64(np.float32(v)) == v and np.float64(np.float16(v)) == v   # exact in both
+        assert np.all(w16[c, 0:2] == (bf | (bf << 16))), c
+        assert np.all(w16[c, 2:4] == (hf | (hf << 16))), c
+        assert np.all(f32[c] == np.float32(v)), c
