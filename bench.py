@@ -22,6 +22,8 @@ of the remaining shapes:
   packed3-decode     B=32, 32/8 heads, 3-bit cache with fp16 (scale, zero), block size 16,
                      contexts U{1k..16k}, fp16 query (KV GB/s)
   pack3-exhaustive   pack3 + unpack3 over all 2^24 octets, with the bijection check
+  fp8-decode         the Llama-8B decode shape over fp8 e4m3fn pools with per-row fp32 scales
+                     (KV GB/s; the pools hold half the bytes of the bf16 ones)
   copy-calibration   a plain device copy of 1 GiB, the reference for HBM byte counters
 """
 from __future__ import annotations
@@ -403,6 +405,68 @@ def run_packed3(args, P, W):
     return rec
 
 
+def run_fp8_decode(args, P, W):
+    """paged_decode at the Llama-8B shape over fp8 e4m3fn pools (one fp32 scale per row),
+    quantised from four bf16 layer pools through kv_append and read in rotation."""
+    import torch
+    pools = []
+    for i in range(N_LAYERS):
+        wl = W.llama8b_decode("cuda", data_seed=W.BASE_SEED + 2 + 1000 * i, poison=False)
+        NB, BS, H, D = wl.k_pool.shape
+        kc = torch.empty((NB, BS, H, D), dtype=torch.uint8, device="cuda")
+        vc = torch.empty_like(kc)
+        km = torch.empty((NB, BS, H), dtype=torch.float32, device="cuda")
+        vm = torch.empty_like(km)
+        slots = torch.arange(NB * BS, dtype=torch.int64, device="cuda")
+        P.kv_append(wl.k_pool.reshape(NB * BS, H, D), wl.v_pool.reshape(NB * BS, H, D), slots,
+                    kc, vc, km, vm)
+        torch.cuda.synchronize()
+        wl.k_pool = wl.v_pool = None               # the bf16 pools are no longer needed
+        pools.append((wl, kc, vc, km, vm))
+    wl0 = pools[0][0]
+    B, Hq, H, D = wl0.batch, wl0.num_q_heads, wl0.num_kv_heads, wl0.head_dim
+    maxctx = max(int(p[0].ctx_before.max()) for p in pools)
+    dev = [dict(bt=w.block_tables.cuda(), ctx=w.ctx_before.cuda(), out=torch.empty_like(w.q)) for w, *_ in pools]
+    ws = P.decode_workspace(B, Hq, H, D, maxctx, args.partition_size)
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        w, kc, vc, km, vm = pools[i % N_LAYERS]
+        d = dev[i % N_LAYERS]
+        P.paged_decode(w.q, kc, vc, d["bt"], d["ctx"], int(w.ctx_before.max()), w.sm_scale,
+                       k_meta=km, v_meta=vm, partition_size=args.partition_size, workspace=ws,
+                       out=d["out"])
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(i)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = event_times_ms(call, args.steps, stream)
+    for d in dev:
+        assert torch.isfinite(d["out"].float()).all(), "non-finite decode output"
+    algs = []
+    for w, *_ in pools:
+        w.ctx_after = w.ctx_before                 # decode only: the pools hold ctx_before tokens
+        algs.append(decode_bytes(w, 2 * (D + 4))[0])   # D codes + one fp32 scale, K and V
+    alg = float(sum(algs) / len(algs))
+    st = stats_us(ms)
+    tokens = int(sum(int(w.ctx_before.sum()) for w, *_ in pools) / N_LAYERS)
+    config = {"workload": "fp8-decode", "batch": B, "num_q_heads": Hq, "num_kv_heads": H,
+              "head_dim": D, "block_size": wl0.block_size, "context": "U{512..4096}",
+              "cache": "fp8 e4m3fn + fp32 per-row scale", "query": "bf16",
+              "layers_rotated": N_LAYERS, "partition_size": args.partition_size or "auto"}
+    rec = base_record(args, "paged decode KV GB/s (fp8 e4m3fn cache)",
+                      alg / (st["mean"] * 1e-6) / 1e9, "GB/s", ms_per_step, "bf16", config)
+    rec.update({"decode_us": st, "context_tokens_per_s": round(tokens / (st["mean"] * 1e-6), 1),
+                "roofline": hbm_roofline("paged_decode (decode_kernel fp8 + merge_kernel)", alg,
+                                         ms.mean() * 1e-3)})
+    return rec
+
+
 def run_pack3_exhaustive(args, P, W):
     """pack3 + unpack3 over every 24-bit octet: values v_j(i) = (i >> 3j) & 7 must pack to
     the three little-endian bytes of i, and unpack back."""
@@ -461,7 +525,8 @@ def run_copy_calibration(args, P, W):
 
 WORKLOADS = {"llama8b-decode-step": run_llama8b, "mixed-append-fp8": run_mixed_append,
              "long-context": run_long_context, "packed3-decode": run_packed3,
-             "pack3-exhaustive": run_pack3_exhaustive, "copy-calibration": run_copy_calibration}
+             "pack3-exhaustive": run_pack3_exhaustive, "copy-calibration": run_copy_calibration,
+             "fp8-decode": run_fp8_decode}
 
 
 def main():
