@@ -148,7 +148,7 @@ def _u3_pools_from_raw(wl, k_all, v_all, slots):
     return pools
 
 
-def _u3_case(P, batch, ctx_lo, ctx_hi, seed, sample=None, qdtype=torch.float16):
+def _u3_case(P, batch, ctx_lo, ctx_hi, seed, sample=None, qdtype=torch.float16, workspace=None):
     wl = W.packed3_decode("cuda", seed=seed, batch=batch, ctx_lo=ctx_lo, ctx_hi=ctx_hi)
     NB, BS, H, D = wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim
     kc = torch.zeros((NB, BS, H, D * 3 // 32), dtype=torch.int32, device="cuda")
@@ -159,7 +159,7 @@ def _u3_case(P, batch, ctx_lo, ctx_hi, seed, sample=None, qdtype=torch.float16):
     q = wl.q.to(qdtype)
     out = P.paged_decode(q, kc, vc, wl.block_tables.cuda(), wl.ctx_after.cuda(),
                          int(wl.ctx_after.max()), wl.sm_scale, k_meta=km, v_meta=vm,
-                         cache_dtype="u3")
+                         cache_dtype="u3", workspace=workspace)
     kpool, vpool = _u3_pools_from_raw(wl, wl.new_k, wl.new_v, wl.slot_mapping)
     assert np.array_equal(np_u32(kc), kpool.cache) and np.array_equal(np_u32(vc), vpool.cache)
     assert np.array_equal(km.cpu().numpy().view(np.uint16), kpool.meta.view(np.uint16))
@@ -374,3 +374,29 @@ def test_fp8_decode_block_claiming_ragged():
         out = P.paged_decode(wl.q, gpu[0], gpu[1], wl.block_tables.cuda(), wl.ctx_after.cuda(),
                              max(lens), wl.sm_scale, k_meta=gpu[2], v_meta=gpu[3], workspace=ws)
         assert report(f"fp8 claims rep {rep}", f32_of(out), want, wl.dtype) <= ATTN_TOL
+
+
+def test_one_workspace_serves_every_cache_kind():
+    """A workspace sized by paged_decode_workspace_size (which plans for every cache kind) serves
+    bf16, fp8 and 3-bit decodes in turn, and the 64-token-block fp8 call with run-time block
+    hand-out in between leaves it usable for the next."""
+    P = need_gpu()
+    lens = [700, 1, 4100, 64, 0, 2048]
+    same = W.decode_workload("mix-same", batch=len(lens), num_q_heads=32, num_kv_heads=8, head_dim=128,
+                             block_size=64, ctx_lo=0, ctx_hi=0, dtype=torch.bfloat16, device="cuda",
+                             seed=W.BASE_SEED + 41, append_one=False, ctx_override=lens)
+    gpu = _fp8_pools_gpu(P, same)
+    live = _live_slots(same, lens)
+    kpool8, vpool8 = _fp8_pools_oracle(same, live)
+    want_same = _oracle_same(same, same.k_pool, same.v_pool, same.ctx_after)
+    want_fp8 = paged_decode_ref(f32_of(same.q), kpool8, vpool8, same.block_tables.numpy(), np.array(lens),
+                                same.block_size, same.num_kv_heads, same.sm_scale)
+    ws = P.decode_workspace(same.batch, same.num_q_heads, same.num_kv_heads, same.head_dim, max(lens), 0)
+    for rep in range(2):
+        out = _decode(P, same, same.k_pool, same.v_pool, same.ctx_after, workspace=ws)
+        assert report(f"mixed kinds bf16 {rep}", f32_of(out), want_same, same.dtype) <= ATTN_TOL
+        out = P.paged_decode(same.q, gpu[0], gpu[1], same.block_tables.cuda(), same.ctx_after.cuda(),
+                             max(lens), same.sm_scale, k_meta=gpu[2], v_meta=gpu[3], workspace=ws)
+        assert report(f"mixed kinds fp8 {rep}", f32_of(out), want_fp8, same.dtype) <= ATTN_TOL
+        got, want = _u3_case(P, batch=3, ctx_lo=100, ctx_hi=900, seed=13 + rep, workspace=ws)
+        assert report(f"mixed kinds u3 {rep}", got, want) <= ATTN_TOL
