@@ -449,7 +449,7 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, State<G>& S, in
 // claims (an even count).
 template <int D, int G, bool BF16, CacheKind KIND, int HPI>
 __device__ __forceinline__ void run_claimed(const DecodeParams& p, State<G>& S, int b, int hg, int nu,
-                                            int* claim, int lane, int tr, int hh, int c, int stream) {
+                                            int* claim, int lane, int tr, int hh, int c) {
   using Gm = Geo<D, HPI, G>;
   using R = Regs<Gm::NI, KIND>;
   constexpr int esz = KIND == CacheKind::U3 ? 4 : KIND == CacheKind::Fp8 ? 1 : 2;
@@ -684,7 +684,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
         const int nu = ctx >> p.log2_claim;
         run_claimed<D, G, BF16, KIND, HPI>(p, S, b, hg, nu,
                                            p.ws_claim + ((int64_t)b * NHG + hg) * kClaimWaves + wv,
-                                           lane, tr, hh, c, stream);
+                                           lane, tr, hh, c);
         if (g1 == n && (nu << p.log2_claim) < ctx) range(nu << p.log2_claim, ctx);
       } else {
         range(t0, t1);
