@@ -24,6 +24,8 @@ of the remaining shapes:
   pack3-exhaustive   pack3 + unpack3 over all 2^24 octets, with the bijection check
   fp8-decode         the Llama-8B decode shape over fp8 e4m3fn pools with per-row fp32 scales
                      (KV GB/s; the pools hold half the bytes of the bf16 ones)
+  dual-stacked-decode  the Llama-8B decode shape over the dual-stacked block layout
+                     [num_blocks, 2, num_kv_heads, block_size, head_dim], as strided views (KV GB/s)
   copy-calibration   a plain device copy of 1 GiB, the reference for HBM byte counters
 """
 from __future__ import annotations
@@ -467,6 +469,62 @@ def run_fp8_decode(args, P, W):
     return rec
 
 
+def run_dual_stacked(args, P, W):
+    """paged_decode at the Llama-8B shape over the dual-stacked block layout
+    [num_blocks, 2, num_kv_heads, block_size, head_dim] (K and V of a block in one buffer,
+    head-major inside the block), passed as two strided views; four layer pools in rotation."""
+    import torch
+    layers = []
+    for i in range(N_LAYERS):
+        wl = W.llama8b_decode("cuda", data_seed=W.BASE_SEED + 2 + 1000 * i, poison=False)
+        NB, BS, H, D = wl.k_pool.shape
+        buf = torch.empty((NB, 2, H, BS, D), dtype=wl.dtype, device="cuda")
+        kc, vc = buf[:, 0].permute(0, 2, 1, 3), buf[:, 1].permute(0, 2, 1, 3)
+        kc.copy_(wl.k_pool)
+        vc.copy_(wl.v_pool)
+        torch.cuda.synchronize()
+        wl.k_pool = wl.v_pool = None
+        layers.append((wl, buf, kc, vc, wl.block_tables.cuda(), wl.ctx_before.cuda(), torch.empty_like(wl.q)))
+    wl0 = layers[0][0]
+    B, Hq, H, D = wl0.batch, wl0.num_q_heads, wl0.num_kv_heads, wl0.head_dim
+    maxctx = max(int(l[0].ctx_before.max()) for l in layers)
+    ws = P.decode_workspace(B, Hq, H, D, maxctx, args.partition_size)
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        w, _, kc, vc, bt, ctx, out = layers[i % N_LAYERS]
+        P.paged_decode(w.q, kc, vc, bt, ctx, int(w.ctx_before.max()), w.sm_scale,
+                       partition_size=args.partition_size, workspace=ws, out=out)
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(i)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = event_times_ms(call, args.steps, stream)
+    for l in layers:
+        assert torch.isfinite(l[6].float()).all(), "non-finite decode output"
+    algs = []
+    for l in layers:
+        w = l[0]
+        w.ctx_after = w.ctx_before
+        algs.append(decode_bytes(w, 2 * D * 2)[0])
+    alg = float(sum(algs) / len(algs))
+    st = stats_us(ms)
+    config = {"workload": "dual-stacked-decode", "batch": B, "num_q_heads": Hq, "num_kv_heads": H,
+              "head_dim": D, "block_size": wl0.block_size, "context": "U{512..4096}",
+              "layout": "[num_blocks, 2, num_kv_heads, block_size, head_dim]", "layers_rotated": N_LAYERS,
+              "partition_size": args.partition_size or "auto"}
+    rec = base_record(args, "paged decode KV GB/s (dual-stacked block layout)",
+                      alg / (st["mean"] * 1e-6) / 1e9, "GB/s", ms_per_step, "bf16", config)
+    rec.update({"decode_us": st, "roofline": hbm_roofline("paged_decode (decode_kernel + merge_kernel)", alg,
+                                                          ms.mean() * 1e-3)})
+    return rec
+
+
 def run_pack3_exhaustive(args, P, W):
     """pack3 + unpack3 over every 24-bit octet: values v_j(i) = (i >> 3j) & 7 must pack to
     the three little-endian bytes of i, and unpack back."""
@@ -526,7 +584,7 @@ def run_copy_calibration(args, P, W):
 WORKLOADS = {"llama8b-decode-step": run_llama8b, "mixed-append-fp8": run_mixed_append,
              "long-context": run_long_context, "packed3-decode": run_packed3,
              "pack3-exhaustive": run_pack3_exhaustive, "copy-calibration": run_copy_calibration,
-             "fp8-decode": run_fp8_decode}
+             "fp8-decode": run_fp8_decode, "dual-stacked-decode": run_dual_stacked}
 
 
 def main():

@@ -400,3 +400,59 @@ def test_one_workspace_serves_every_cache_kind():
         assert report(f"mixed kinds fp8 {rep}", f32_of(out), want_fp8, same.dtype) <= ATTN_TOL
         got, want = _u3_case(P, batch=3, ctx_lo=100, ctx_hi=900, seed=13 + rep, workspace=ws)
         assert report(f"mixed kinds u3 {rep}", got, want) <= ATTN_TOL
+
+
+@pytest.mark.parametrize("kind", ["same", "fp8"])
+def test_dual_stacked_block_layout(kind):
+    """The dual-stacked block layout [num_blocks, 2, num_kv_heads, block_size, head_dim] (K and V
+    of a block in one buffer, head-major inside the block) through the stride arguments: K and V
+    are the two views buf[:, 0] and buf[:, 1] permuted to [block, slot, head, d]; append then
+    decode, against the oracle on the same rows."""
+    P = need_gpu()
+    lens = [300, 17, 1025, 0, 64]
+    wl = W.decode_workload("dual-stacked", batch=len(lens), num_q_heads=16, num_kv_heads=4, head_dim=128,
+                           block_size=16, ctx_lo=0, ctx_hi=0, dtype=torch.bfloat16, device="cuda",
+                           seed=W.BASE_SEED + 51, append_one=True, ctx_override=lens, poison=False)
+    NB, BS, H, D = wl.k_pool.shape
+    if kind == "same":
+        buf = torch.empty((NB, 2, H, BS, D), dtype=wl.dtype, device="cuda")
+        kc, vc = buf[:, 0].permute(0, 2, 1, 3), buf[:, 1].permute(0, 2, 1, 3)
+        kc.copy_(wl.k_pool)
+        vc.copy_(wl.v_pool)
+        km = vm = None
+    else:
+        gpu = _fp8_pools_gpu(P, wl)
+        buf = torch.empty((NB, 2, H, BS, D), dtype=torch.uint8, device="cuda")
+        kc, vc = buf[:, 0].permute(0, 2, 1, 3), buf[:, 1].permute(0, 2, 1, 3)
+        kc.copy_(gpu[0])
+        vc.copy_(gpu[1])
+        km, vm = gpu[2], gpu[3]
+    assert kc.stride() == (2 * H * BS * D, D, BS * D, 1)
+    # the new token of every request through the strided pools
+    if kind == "same":
+        P.kv_append(wl.new_k, wl.new_v, wl.slot_mapping.cuda(), kc, vc)
+        dn = dtype_name(wl.dtype)
+        kpool = PoolView("same", bits16(kc), dtype=dn)
+        vpool = PoolView("same", bits16(vc), dtype=dn)
+        kref, vref = bits16(wl.k_pool).copy(), bits16(wl.v_pool).copy()
+        oracle.append_ref(bits16(wl.new_k), bits16(wl.new_v), wl.slot_mapping.numpy(), kref, vref,
+                          oracle.CacheSpec("same", dn), BS)
+        assert np.array_equal(kpool.cache, kref) and np.array_equal(vpool.cache, vref)
+    else:
+        P.kv_append(wl.new_k, wl.new_v, wl.slot_mapping.cuda(), kc, vc, km, vm)
+        lens_after = wl.ctx_after.numpy()
+        live = _live_slots(wl, lens_after)
+        # oracle pools: its own quantisation of the live bf16 rows, the new tokens included
+        kraw, vraw = wl.k_pool.clone(), wl.v_pool.clone()
+        sl = wl.slot_mapping.cuda()
+        kraw.view(NB * BS, H, D)[sl] = wl.new_k
+        vraw.view(NB * BS, H, D)[sl] = wl.new_v
+        raw = W.PagedWorkload(**{**wl.__dict__, "k_pool": kraw, "v_pool": vraw})
+        kpool, vpool = _fp8_pools_oracle(raw, live)
+        assert np.array_equal(kc.cpu().numpy()[live], kpool.cache[live])
+        assert np.array_equal(vc.cpu().numpy()[live], vpool.cache[live])
+    out = P.paged_decode(wl.q, kc, vc, wl.block_tables.cuda(), wl.ctx_after.cuda(), int(wl.ctx_after.max()),
+                         wl.sm_scale, k_meta=km, v_meta=vm)
+    want = paged_decode_ref(f32_of(wl.q), kpool, vpool, wl.block_tables.numpy(), wl.ctx_after.numpy(),
+                            BS, H, wl.sm_scale)
+    assert report(f"dual-stacked {kind}", f32_of(out), want, wl.dtype) <= ATTN_TOL
