@@ -405,9 +405,10 @@ def test_one_workspace_serves_every_cache_kind():
 @pytest.mark.parametrize("kind", ["same", "fp8"])
 def test_dual_stacked_block_layout(kind):
     """The dual-stacked block layout [num_blocks, 2, num_kv_heads, block_size, head_dim] (K and V
-    of a block in one buffer, head-major inside the block) through the stride arguments: K and V
-    are the two views buf[:, 0] and buf[:, 1] permuted to [block, slot, head, d]; append then
-    decode, against the oracle on the same rows."""
+    of a block in one buffer, head-major inside the block; "Write Triton Kv Cache Append Kernel",
+    Inputs (cache layout) and Common failure modes) through the stride arguments: K and V are the
+    two views buf[:, 0] and buf[:, 1] permuted to [block, slot, head, d]; append then decode,
+    against the oracle on the same rows."""
     P = need_gpu()
     lens = [300, 17, 1025, 0, 64]
     wl = W.decode_workload("dual-stacked", batch=len(lens), num_q_heads=16, num_kv_heads=4, head_dim=128,
