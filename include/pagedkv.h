@@ -77,7 +77,13 @@ typedef enum {
  *                    head_dim elements (F16/BF16/FP8) or head_dim*3/32 uint32 words
  *                    (U3); row (blk, slot, h) at blk*c_stride_block +
  *                    c_stride_slot*slot + c_stride_head*h.  16-byte aligned rows
- *                    (8-byte for U3 with head_dim 64).
+ *                    (8-byte for U3 with head_dim 64).  Any strides of that form are
+ *                    accepted, e.g. the dual-stacked block layout [num_blocks, 2,
+ *                    num_kv_heads, block_size, head_dim] as two views (k_cache = base,
+ *                    v_cache = base + num_kv_heads*block_size*head_dim, c_stride_block =
+ *                    2*num_kv_heads*block_size*head_dim, c_stride_slot = head_dim,
+ *                    c_stride_head = block_size*head_dim); k_cache and v_cache share the
+ *                    strides.
  *   cache_dtype      == in_dtype (bit copy), or PKV_FP8_E4M3FN, or PKV_U3.
  *   k_meta, v_meta   FP8: fp32 [num_blocks, block_size, num_kv_heads] per-row scales
  *                    (s = absmax/448, 1 for an all-zero row; code = RNE_e4m3fn(
