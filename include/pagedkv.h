@@ -112,11 +112,11 @@ int kv_append(const void* k_new, const void* v_new, pkv_dtype in_dtype,
  * Split-K ("flash-decoding", named by [3bit] in its title paragraph as the form of its fused
  * decode): the context of each (request, kv head) may be cut into token ranges that are
  * reduced independently and merged by log-sum-exp.  The library balances the work by
- * giving each resident workgroup of the current device an equal share of all
- * (request, kv head, granule) units, where a granule is `partition_size` tokens; a context
- * is cut at multiples of the granule, except that where a block of the cache holds at least
- * 64 KB of a wave's K/V the workgroups sharing a context hand its blocks out among
- * themselves at run time.  The workspace holds the partial states of the ranges that get
+ * giving each resident workgroup of the current device a share of all (request, kv head,
+ * granule) units sized to its expected speed, where a granule is `partition_size` tokens;
+ * a context is cut at multiples of the granule, except that where a block of the cache
+ * holds at least 64 KB of a wave's K/V the workgroups sharing a context hand its blocks out
+ * among themselves at run time, in pieces of up to 32 tokens.  The workspace holds the partial states of the ranges that get
  * cut, so its size depends on the current device's compute-unit count: query it on the
  * device that will run the call.
  * partition_size: 0 = automatic (16 tokens, the finest balance), else a multiple of 16.
