@@ -305,12 +305,13 @@ int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
   p.ws_ml = reinterpret_cast<float*>(ws + L.ml_off);
   p.ws_seg = reinterpret_cast<int*>(ws + L.seg_off);
   p.ws_claim = reinterpret_cast<int*>(ws + L.claim_off);
-  // Block claiming: a wave can only take whole blocks, and its share of the bandwidth is small
-  // (~1/2000 of the device), so a claim of B bytes keeps it busy for ~B / 3 GB/s.  It pays only
-  // where blocks are large enough for the claims to outweigh their cost and coarse enough split
-  // granules leave a tail (measured: 128 KB blocks of the long-context decode gain ~10 %, 32 KB
-  // blocks of the Llama-8B step lose 15 %): at least 64 KB of K/V per wave and block.  It also
-  // needs an even number of chunks per block and at most 4 head waves.
+  // Block claiming: a wave takes whole claim units (kClaimUnitChunks chunks inside one block,
+  // or whole blocks), and its share of the bandwidth is small (~1/2000 of the device), so a
+  // claim of B bytes keeps it busy for ~B / 3 GB/s, and every claim is a device-scope atomic.
+  // It pays only where blocks are large enough for the claims to outweigh their cost and
+  // coarse enough split granules leave a tail (measured: 128 KB blocks of the long-context
+  // decode gain ~10 %, 32 KB blocks of the Llama-8B step lose 15 %): at least 64 KB of K/V per
+  // wave and block.  It also needs an even number of chunks per unit and at most 4 head waves.
   const int64_t row_bytes = cache_dtype == PKV_U3    ? 2 * (head_dim * 3 / 8 + 4)
                             : cache_dtype == PKV_FP8_E4M3FN ? 2 * (int64_t)(head_dim + 4)
                                                             : 4 * (int64_t)head_dim;

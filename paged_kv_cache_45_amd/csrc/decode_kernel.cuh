@@ -8,7 +8,9 @@
 // accumulator).  GQA ("Write Triton Kv Cache Append Kernel", Kernel design rules): the G =
 // Hq / Hkv query heads h = kvh*G .. kvh*G+G-1 share kv head kvh.  The 3-bit cache
 // ("triton-3bit-kv-cache-kernel" README, title paragraph and section 2) is unpacked and
-// dequantised, x = (q - z) * s, in registers.  Split-K: the context of a (request, kv head)
+// dequantised, x = (q - z) * s, in registers; the fp8 e4m3fn cache reads as decode(code) * s
+// with the row's scale (the inverse of the append's quantiser, "Write Triton Kv Cache Append
+// Kernel", Correctness requirements).  Split-K: the context of a (request, kv head)
 // may be cut at multiples of the partition size into ranges that are reduced separately
 // and merged by log-sum-exp (the flash-decoding form the 3-bit README names).
 //
@@ -18,7 +20,8 @@
 //    token (1 KB for 4 heads of 128 bf16), and the waves of a workgroup cover the other
 //    heads of the same tokens at the same time, so whole slot rows are streamed and each
 //    opened DRAM page is used in full.  Lane layout: D/8 lanes per (head, token) row, each
-//    lane owning 8 consecutive elements (one 16-byte load of K and one of V).
+//    lane owning 8 consecutive elements (one 16-byte load of K and one of V; 8 bytes of
+//    codes for fp8).  The K/V stream is loaded with the non-temporal hint: it is read once.
 //  * Work (stream-K): requests are cut into granules of `partition_size` tokens; the
 //    (request, head group, granule) units are laid end to end and the grid holds as many
 //    workgroups as the chip keeps resident, each taking a contiguous range of units sized
