@@ -457,3 +457,21 @@ def test_dual_stacked_block_layout(kind):
     want = paged_decode_ref(f32_of(wl.q), kpool, vpool, wl.block_tables.numpy(), wl.ctx_after.numpy(),
                             BS, H, wl.sm_scale)
     assert report(f"dual-stacked {kind}", f32_of(out), want, wl.dtype) <= ATTN_TOL
+
+
+def test_max_batch_ragged():
+    """The largest batch the ABI accepts (8192 requests): the per-workgroup prefix of context
+    lengths is built over several passes of the workgroup's threads, and contexts of 0 and a
+    few tokens are mixed; every row against the oracle."""
+    P = need_gpu()
+    B = 8192
+    wl = W.decode_workload("max-batch", batch=B, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                           block_size=16, ctx_lo=0, ctx_hi=40, dtype=torch.float16, device="cuda",
+                           seed=W.BASE_SEED + 61, append_one=False)
+    assert int((wl.ctx_after == 0).sum()) > 0
+    want = _oracle_same(wl, wl.k_pool, wl.v_pool, wl.ctx_after)
+    for ps in (0, 32):
+        out = _decode(P, wl, wl.k_pool, wl.v_pool, wl.ctx_after, partition_size=ps)
+        got = f32_of(out)
+        assert np.all(got[wl.ctx_after.numpy() == 0] == 0)
+        assert report(f"max batch ps{ps}", got, want, wl.dtype) <= ATTN_TOL
