@@ -475,3 +475,33 @@ def test_max_batch_ragged():
         got = f32_of(out)
         assert np.all(got[wl.ctx_after.numpy() == 0] == 0)
         assert report(f"max batch ps{ps}", got, want, wl.dtype) <= ATTN_TOL
+
+
+@pytest.mark.parametrize("G", [1, 8])
+@pytest.mark.parametrize("D,bs", [(128, 16), (64, 64)])
+def test_u3_decode_shapes_ragged(G, D, bs):
+    """3-bit pools (quantised and packed by the oracle, uploaded as they are) at group sizes and
+    head dims the full-size cases do not use; ragged and empty contexts, two partition sizes."""
+    P = need_gpu()
+    Hkv = 2
+    lens = [1, 15, 16, 17, 511, 512, 513, 1000, 0, 33]
+    wl = W.decode_workload("u3-ragged", batch=len(lens), num_q_heads=G * Hkv, num_kv_heads=Hkv,
+                           head_dim=D, block_size=bs, ctx_lo=0, ctx_hi=0, dtype=torch.float16,
+                           device="cuda", seed=300 + G + D + bs, append_one=False, ctx_override=lens,
+                           poison=False)
+    NB, BS, H, _ = wl.k_pool.shape
+    slots = torch.arange(NB * BS, dtype=torch.int64)
+    kpool, vpool = _u3_pools_from_raw(wl, wl.k_pool.reshape(NB * BS, H, D), wl.v_pool.reshape(NB * BS, H, D),
+                                      slots)
+    kc = torch.from_numpy(kpool.cache.view(np.int32)).cuda()
+    vc = torch.from_numpy(vpool.cache.view(np.int32)).cuda()
+    km = torch.from_numpy(kpool.meta).cuda()
+    vm = torch.from_numpy(vpool.meta).cuda()
+    want = paged_decode_ref(f32_of(wl.q), kpool, vpool, wl.block_tables.numpy(), np.array(lens), bs, Hkv,
+                            wl.sm_scale)
+    for ps in (0, 512):
+        out = P.paged_decode(wl.q, kc, vc, wl.block_tables.cuda(), wl.ctx_after.cuda(), max(lens),
+                             wl.sm_scale, k_meta=km, v_meta=vm, partition_size=ps, cache_dtype="u3")
+        got = f32_of(out)
+        assert np.all(got[lens.index(0)] == 0)
+        assert report(f"u3 G{G} D{D} bs{bs} ps{ps}", got, want, torch.float16) <= ATTN_TOL
