@@ -24,6 +24,9 @@ from .pack3 import (pack3, unpack3, pack3_words, unpack3_words, pack_rows_u3,
 from .fp8 import (e4m3fn_decode_table, e4m3fn_encode_rne, e4m3fn_decode,
                   quantize_fp8_rows, dequantize_fp8_rows, E4M3_MAX)
 from .quant3 import quantize_u3_rows, dequantize_u3_rows
+from .quant8 import (e5m2_decode_table, e5m2_decode, e5m2_encode_rne, quantize_e5m2_rows,
+                     quantize_int8_rows, dequantize_e5m2_rows, dequantize_int8_rows, E5M2_MAX,
+                     INT8_MAX)
 from .slots import decode_slot_mapping, prefill_slot_mapping
 from .append import append_ref, CacheSpec
 from .attention import (paged_decode_ref, paged_decode_split_ref, lse_merge_ref,
@@ -33,6 +36,8 @@ __all__ = [
     "pack3", "unpack3", "pack3_words", "unpack3_words", "pack_rows_u3", "unpack_rows_u3",
     "e4m3fn_decode_table", "e4m3fn_encode_rne", "e4m3fn_decode", "quantize_fp8_rows",
     "dequantize_fp8_rows", "E4M3_MAX", "quantize_u3_rows", "dequantize_u3_rows",
+    "e5m2_decode_table", "e5m2_decode", "e5m2_encode_rne", "quantize_e5m2_rows",
+    "quantize_int8_rows", "dequantize_e5m2_rows", "dequantize_int8_rows", "E5M2_MAX", "INT8_MAX",
     "decode_slot_mapping", "prefill_slot_mapping", "append_ref", "CacheSpec",
     "paged_decode_ref", "paged_decode_split_ref", "lse_merge_ref", "gather_rows_f64", "PoolView",
 ]

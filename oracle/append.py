@@ -14,6 +14,8 @@ Pages cited: [Append] "Write Triton Kv Cache Append Kernel" (skillsdirectory.com
 Cache element types:
   "same"  - the cache has the input's dtype; the row is copied bit for bit,
   "fp8"   - e4m3fn codes, with one fp32 scale per (block, slot, kv head),
+  "e5m2"  - e5m2 codes, scaled the same way (oracle/quant8.py),
+  "i8"    - int8 codes (stored as their bytes), scaled the same way (oracle/quant8.py),
   "u3"    - 3-bit codes packed 32 per 3 uint32 words (head_dim*3/32 words per
             row), with an fp16 (scale, zero) pair per (block, slot, kv head).
 
@@ -31,13 +33,14 @@ from typing import Optional
 import numpy as np
 
 from .fp8 import quantize_fp8_rows
+from .quant8 import quantize_e5m2_rows, quantize_int8_rows
 from .quant3 import quantize_u3_rows
 from .pack3 import pack_rows_u3
 
 
 @dataclasses.dataclass
 class CacheSpec:
-    kind: str                 # "same" | "fp8" | "u3"
+    kind: str                 # "same" | "fp8" | "e5m2" | "i8" | "u3"
     in_dtype: str             # "f16" | "bf16"
 
 
@@ -57,9 +60,9 @@ def append_ref(k_new_bits: np.ndarray, v_new_bits: np.ndarray, slot_mapping: np.
     """Update the caches in place.
 
     k_new_bits, v_new_bits: uint16 [T, Hkv, D] (the raw fp16/bf16 bits).
-    k_cache, v_cache: "same": uint16 [NB, BS, Hkv, D]; "fp8": uint8 [NB, BS, Hkv, D];
+    k_cache, v_cache: "same": uint16 [NB, BS, Hkv, D]; "fp8", "e5m2", "i8": uint8 [NB, BS, Hkv, D];
                       "u3": uint32 [NB, BS, Hkv, 3*D/32].
-    k_meta, v_meta:   "fp8": float32 [NB, BS, Hkv]; "u3": float16 [NB, BS, Hkv, 2].
+    k_meta, v_meta:   "fp8", "e5m2", "i8": float32 [NB, BS, Hkv]; "u3": float16 [NB, BS, Hkv, 2].
     """
     nb = k_cache.shape[0]
     T = slot_mapping.shape[0]
@@ -75,6 +78,11 @@ def append_ref(k_new_bits: np.ndarray, v_new_bits: np.ndarray, slot_mapping: np.
             elif spec.kind == "fp8":
                 codes, scale = quantize_fp8_rows(to_f32(row_bits, spec.in_dtype))
                 cache[blk, off] = codes
+                meta[blk, off] = scale
+            elif spec.kind in ("e5m2", "i8"):
+                quant = quantize_e5m2_rows if spec.kind == "e5m2" else quantize_int8_rows
+                codes, scale = quant(to_f32(row_bits, spec.in_dtype))
+                cache[blk, off] = codes.view(np.uint8)
                 meta[blk, off] = scale
             elif spec.kind == "u3":
                 q, s16, z16 = quantize_u3_rows(to_f32(row_bits, spec.in_dtype))

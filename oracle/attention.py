@@ -31,6 +31,7 @@ import numpy as np
 
 from .append import to_f32
 from .fp8 import dequantize_fp8_rows
+from .quant8 import dequantize_e5m2_rows, dequantize_int8_rows
 from .pack3 import unpack_rows_u3
 from .quant3 import dequantize_u3_rows
 
@@ -51,6 +52,10 @@ class PoolView:
             out = to_f32(c, self.dtype).astype(np.float64)
         elif self.kind == "fp8":
             out = dequantize_fp8_rows(c, self.meta[blocks, :, kv_head])
+        elif self.kind == "e5m2":
+            out = dequantize_e5m2_rows(c, self.meta[blocks, :, kv_head])
+        elif self.kind == "i8":
+            out = dequantize_int8_rows(c, self.meta[blocks, :, kv_head])
         elif self.kind == "u3":
             q = unpack_rows_u3(c, self.head_dim)
             m = self.meta[blocks, :, kv_head]

@@ -14,6 +14,7 @@ import torch
 from paged_kv_cache_45_amd import workloads as W
 from oracle import (decode_slot_mapping, prefill_slot_mapping, append_ref, CacheSpec,
                     paged_decode_ref, PoolView, quantize_fp8_rows, quantize_u3_rows,
+                    quantize_e5m2_rows, quantize_int8_rows,
                     pack_rows_u3)
 from oracle.append import to_f32
 
@@ -99,14 +100,14 @@ def test_append_readback_padding_untouched_idempotent():
     assert np.array_equal(k3, k0)
 
 
-@pytest.mark.parametrize("kind", ["fp8", "u3"])
+@pytest.mark.parametrize("kind", ["fp8", "e5m2", "i8", "u3"])
 def test_quantised_append_matches_row_quantiser(kind):
     wl = W.mixed_append("cpu", num_prompts=1, prompt_lo=40, prompt_hi=40, num_decode=3,
                         ctx_lo=5, ctx_hi=30, block_size=16, head_dim=128, num_kv_heads=2)
     nb, BS, H, D = wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim
     nk, nv = _bits(wl.new_k), _bits(wl.new_v)
     slots = wl.slot_mapping.numpy()
-    if kind == "fp8":
+    if kind in ("fp8", "e5m2", "i8"):
         k = np.zeros((nb, BS, H, D), np.uint8)
         km = np.zeros((nb, BS, H), np.float32)
     else:
@@ -122,6 +123,9 @@ def test_quantised_append_matches_row_quantiser(kind):
         if kind == "fp8":
             codes, sc = quantize_fp8_rows(x)
             assert np.array_equal(k[blk, off], codes) and np.array_equal(km[blk, off], sc)
+        elif kind in ("e5m2", "i8"):
+            codes, sc = (quantize_e5m2_rows if kind == "e5m2" else quantize_int8_rows)(x)
+            assert np.array_equal(k[blk, off], codes.view(np.uint8)) and np.array_equal(km[blk, off], sc)
         else:
             q, s16, z16 = quantize_u3_rows(x)
             assert np.array_equal(k[blk, off], pack_rows_u3(q))
