@@ -23,6 +23,8 @@ of the remaining shapes:
                      contexts U{1k..16k}, fp16 query (KV GB/s)
   pack3-exhaustive   pack3 + unpack3 over all 2^24 octets, with the bijection check
   fp8-decode         the Llama-8B decode shape over fp8 e4m3fn pools with per-row fp32 scales
+  e5m2-decode        the same over fp8 e5m2 pools
+  int8-decode        the same over int8 pools
                      (KV GB/s; the pools hold half the bytes of the bf16 ones)
   dual-stacked-decode  the Llama-8B decode shape over the dual-stacked block layout
                      [num_blocks, 2, num_kv_heads, block_size, head_dim], as strided views (KV GB/s)
@@ -433,10 +435,16 @@ def run_packed3(args, P, W):
     return rec
 
 
-def run_fp8_decode(args, P, W):
-    """paged_decode at the Llama-8B shape over fp8 e4m3fn pools (one fp32 scale per row),
-    quantised from four bf16 layer pools through kv_append and read in rotation."""
+BYTE_CACHES = {"fp8": ("fp8-decode", "fp8 e4m3fn"), "e5m2": ("e5m2-decode", "fp8 e5m2"),
+               "i8": ("int8-decode", "int8")}
+
+
+def run_fp8_decode(args, P, W, kind="fp8"):
+    """paged_decode at the Llama-8B shape over byte-code pools (fp8 e4m3fn, fp8 e5m2 or int8,
+    one fp32 scale per row), quantised from four bf16 layer pools through kv_append and read in
+    rotation."""
     import torch
+    name, label = BYTE_CACHES[kind]
     pools = []
     for i in range(N_LAYERS):
         wl = W.llama8b_decode("cuda", data_seed=W.BASE_SEED + 2 + 1000 * i, poison=False)
@@ -447,7 +455,7 @@ def run_fp8_decode(args, P, W):
         vm = torch.empty_like(km)
         slots = torch.arange(NB * BS, dtype=torch.int64, device="cuda")
         P.kv_append(wl.k_pool.reshape(NB * BS, H, D), wl.v_pool.reshape(NB * BS, H, D), slots,
-                    kc, vc, km, vm)
+                    kc, vc, km, vm, cache_dtype=kind)
         torch.cuda.synchronize()
         wl.k_pool = wl.v_pool = None               # the bf16 pools are no longer needed
         pools.append((wl, kc, vc, km, vm))
@@ -463,7 +471,7 @@ def run_fp8_decode(args, P, W):
         d = dev[i % N_LAYERS]
         P.paged_decode(w.q, kc, vc, d["bt"], d["ctx"], int(w.ctx_before.max()), w.sm_scale,
                        k_meta=km, v_meta=vm, partition_size=args.partition_size, workspace=ws,
-                       out=d["out"])
+                       out=d["out"], cache_dtype=kind)
 
     for i in range(args.warmup):
         call(i)
@@ -483,14 +491,14 @@ def run_fp8_decode(args, P, W):
     alg = float(sum(algs) / len(algs))
     st = stats_us(ms)
     tokens = int(sum(int(w.ctx_before.sum()) for w, *_ in pools) / N_LAYERS)
-    config = {"workload": "fp8-decode", "batch": B, "num_q_heads": Hq, "num_kv_heads": H,
+    config = {"workload": name, "batch": B, "num_q_heads": Hq, "num_kv_heads": H,
               "head_dim": D, "block_size": wl0.block_size, "context": "U{512..4096}",
-              "cache": "fp8 e4m3fn + fp32 per-row scale", "query": "bf16",
+              "cache": f"{label} + fp32 per-row scale", "query": "bf16",
               "layers_rotated": N_LAYERS, "partition_size": args.partition_size or "auto"}
-    rec = base_record(args, "paged decode KV GB/s (fp8 e4m3fn cache)",
+    rec = base_record(args, f"paged decode KV GB/s ({label} cache)",
                       alg / (st["mean"] * 1e-6) / 1e9, "GB/s", ms_per_step, "bf16", config)
     rec.update({"decode_us": st, "context_tokens_per_s": round(tokens / (st["mean"] * 1e-6), 1),
-                "roofline": hbm_roofline("paged_decode (decode_kernel fp8 + merge_kernel)", alg,
+                "roofline": hbm_roofline(f"paged_decode (decode_kernel {kind} + merge_kernel)", alg,
                                          ms.mean() * 1e-3)})
     return rec
 
@@ -610,7 +618,9 @@ def run_copy_calibration(args, P, W):
 WORKLOADS = {"llama8b-decode-step": run_llama8b, "mixed-append-fp8": run_mixed_append,
              "long-context": run_long_context, "packed3-decode": run_packed3,
              "pack3-exhaustive": run_pack3_exhaustive, "copy-calibration": run_copy_calibration,
-             "fp8-decode": run_fp8_decode, "dual-stacked-decode": run_dual_stacked}
+             "fp8-decode": run_fp8_decode, "dual-stacked-decode": run_dual_stacked,
+             "e5m2-decode": lambda a, P, W: run_fp8_decode(a, P, W, "e5m2"),
+             "int8-decode": lambda a, P, W: run_fp8_decode(a, P, W, "i8")}
 
 
 def main():

@@ -53,7 +53,9 @@ typedef enum {
   PKV_F16 = 0,         /* IEEE binary16                                             */
   PKV_BF16 = 1,        /* bfloat16                                                  */
   PKV_FP8_E4M3FN = 2,  /* OCP FP8 E4M3 (finite-only, max 448), one fp32 scale per row */
-  PKV_U3 = 3           /* 3-bit affine codes, 32 per 3 uint32 words, fp16 (scale, zero) per row */
+  PKV_U3 = 3,          /* 3-bit affine codes, 32 per 3 uint32 words, fp16 (scale, zero) per row */
+  PKV_FP8_E5M2 = 4,    /* OCP FP8 E5M2 (bias 15, max finite 57344), one fp32 scale per row  */
+  PKV_INT8 = 5         /* signed 8-bit integers in [-127, 127], one fp32 scale per row      */
 } pkv_dtype;
 
 /*
@@ -62,8 +64,9 @@ typedef enum {
  * Defined by [Append], Required reasoning process steps 1-8 (unified prefill and
  * decode interface; slot = block_id * block_size + slot_in_block; slot < 0 is a
  * no-op taken before any load; K and V in one pass; scale division in fp32 before
- * the cast), Inputs items 1-9, Kernel design rules; the packed 3-bit cache by
- * [3bit], sections 1A/1B (bit layout) and 2, test 3 (fp16 affine scale/zero).
+ * the cast), Inputs items 1-9, Kernel design rules; the fp8 e4m3 / e5m2 and int8 caches
+ * by [Append], Inputs item 4 and step 6; the packed 3-bit cache by [3bit], sections 1A/1B
+ * (bit layout) and 2, test 3 (fp16 affine scale/zero).
  *
  *   k_new, v_new     device, [num_tokens, num_kv_heads, head_dim] of in_dtype (F16
  *                    or BF16); element (t, h, d) at t*stride_tok + h*stride_head + d.
@@ -74,7 +77,7 @@ typedef enum {
  *                    (a caller error, handled defensively).  Two tokens with the same
  *                    slot in one call: undefined which one wins.
  *   k_cache, v_cache device pools [num_blocks, block_size, num_kv_heads, R] where R is
- *                    head_dim elements (F16/BF16/FP8) or head_dim*3/32 uint32 words
+ *                    head_dim elements (F16/BF16, or bytes for FP8/INT8) or head_dim*3/32 uint32 words
  *                    (U3); row (blk, slot, h) at blk*c_stride_block +
  *                    c_stride_slot*slot + c_stride_head*h.  16-byte aligned rows
  *                    (8-byte for U3 with head_dim 64).  Any strides of that form are
@@ -84,10 +87,14 @@ typedef enum {
  *                    2*num_kv_heads*block_size*head_dim, c_stride_slot = head_dim,
  *                    c_stride_head = block_size*head_dim); k_cache and v_cache share the
  *                    strides.
- *   cache_dtype      == in_dtype (bit copy), or PKV_FP8_E4M3FN, or PKV_U3.
- *   k_meta, v_meta   FP8: fp32 [num_blocks, block_size, num_kv_heads] per-row scales
- *                    (s = absmax/448, 1 for an all-zero row; code = RNE_e4m3fn(
- *                    clamp(x/s, +-448))).  U3: fp16 [num_blocks, block_size,
+ *   cache_dtype      == in_dtype (bit copy), or PKV_FP8_E4M3FN, PKV_FP8_E5M2, PKV_INT8
+ *                    (the byte-code caches: pools 8-byte aligned, strides multiples of 8),
+ *                    or PKV_U3.
+ *   k_meta, v_meta   byte-code caches: fp32 [num_blocks, block_size, num_kv_heads] per-row
+ *                    scales s = absmax/M with M = 448 (E4M3FN), 57344 (E5M2) or 127
+ *                    (INT8), s = 1 for an all-zero row; y = clamp(x/s, +-M) with the
+ *                    correctly rounded fp32 quotient; code = RNE_e4m3fn(y), RNE_e5m2(y) or
+ *                    rint(y) (ties to even).  U3: fp16 [num_blocks, block_size,
  *                    num_kv_heads, 2] = (s, z), per-row min/max affine parameters
  *                    (s = fp16((max-min)/7), z = fp16(-min/s), q = clamp(rint(x/s+z),
  *                    0, 7); degenerate rows use s = 1, z = fp16(-min)).  Contiguous.
@@ -134,17 +141,19 @@ size_t paged_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads,
  * block_size] at slot t % block_size; GQA per [Append] (query head h reads kv head
  * h / (num_q_heads / num_kv_heads)); with the 3-bit cache the codes are unpacked and
  * dequantised, x = (q - z) * s, on the fly ([3bit], title paragraph, section 2 test 3);
- * with the fp8 cache each row reads as decode_e4m3fn(code) * s, the inverse of the
- * kv_append quantiser ([Append], Correctness requirements: the quantised cache is read back
- * through the row's scale), with s applied to the row's dot product and to its probability.
+ * with a byte-code cache (fp8 e4m3fn, fp8 e5m2, int8) each row reads as decode(code) * s,
+ * the inverse of the kv_append quantiser ([Append], Inputs item 4 and Correctness
+ * requirements: the quantised cache is read back through the row's scale), with s applied to
+ * the row's dot product and to its probability.
  *
  *   out, q           device [batch, num_q_heads, head_dim] of q_dtype (F16 or BF16);
  *                    element (b, h, d) at b*stride_b + h*stride_h + d; out has the
  *                    same dtype.  16-byte aligned rows.
  *   k_cache, v_cache pools as for kv_append; cache_dtype == q_dtype, or PKV_U3 (with
- *                    k_meta, v_meta fp16 (s, z) as for kv_append), or PKV_FP8_E4M3FN (with
- *                    k_meta, v_meta fp32 per-row scales as for kv_append; pools 8-byte
- *                    aligned, strides multiples of 8, else PKV_EINVAL).
+ *                    k_meta, v_meta fp16 (s, z) as for kv_append), or PKV_FP8_E4M3FN,
+ *                    PKV_FP8_E5M2 or PKV_INT8 (with k_meta, v_meta fp32 per-row scales as
+ *                    for kv_append; pools 8-byte aligned, strides multiples of 8, else
+ *                    PKV_EINVAL).
  *   block_tables     device int32 [batch, bt_stride_b >= cdiv(max_context_len,
  *                    block_size)]; entries at or beyond cdiv(context_lens[b],
  *                    block_size) are never read.  Entries must be < num_blocks.

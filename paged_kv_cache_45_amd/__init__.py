@@ -19,9 +19,10 @@ from typing import Optional
 
 __all__ = ["kv_append", "paged_decode", "paged_decode_workspace_size", "pack3", "unpack3",
            "pkv_status_string", "decode_workspace", "library_path", "load_library",
-           "PKV_F16", "PKV_BF16", "PKV_FP8_E4M3FN", "PKV_U3", "PagedKVError"]
+           "PKV_F16", "PKV_BF16", "PKV_FP8_E4M3FN", "PKV_U3", "PKV_FP8_E5M2", "PKV_INT8",
+           "PagedKVError"]
 
-PKV_F16, PKV_BF16, PKV_FP8_E4M3FN, PKV_U3 = 0, 1, 2, 3
+PKV_F16, PKV_BF16, PKV_FP8_E4M3FN, PKV_U3, PKV_FP8_E5M2, PKV_INT8 = 0, 1, 2, 3, 4, 5
 _STATUS = {0: "PKV_OK", -1: "PKV_EINVAL", -2: "PKV_EUNSUPPORTED", -3: "PKV_EWORKSPACE",
            -4: "PKV_EHIP"}
 
@@ -102,11 +103,16 @@ def _dtype16(t) -> int:
 def _cache_dtype(cache, ref_dtype: int, cache_dtype) -> int:
     import torch
     if cache_dtype is not None:
-        return {"same": ref_dtype, "fp8": PKV_FP8_E4M3FN, "u3": PKV_U3}.get(cache_dtype, cache_dtype)
+        return {"same": ref_dtype, "fp8": PKV_FP8_E4M3FN, "e5m2": PKV_FP8_E5M2, "i8": PKV_INT8,
+                "u3": PKV_U3}.get(cache_dtype, cache_dtype)
     if cache.dtype in (torch.float16, torch.bfloat16):
         return _dtype16(cache)
     if cache.dtype in (torch.uint8, torch.float8_e4m3fn):
         return PKV_FP8_E4M3FN
+    if cache.dtype == torch.float8_e5m2:
+        return PKV_FP8_E5M2
+    if cache.dtype == torch.int8:
+        return PKV_INT8
     if cache.dtype in (torch.int32, torch.uint32):
         return PKV_U3
     raise TypeError(f"cannot infer the cache dtype from {cache.dtype}")
@@ -124,7 +130,8 @@ def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_meta=None, v_meta=
               cache_dtype=None, stream=None) -> None:
     """Write new K/V [T, Hkv, D] into the paged pools through slot_mapping (int64 [T]).
 
-    Caches: [NB, BS, Hkv, D] (same dtype as the input, or uint8 fp8 codes with fp32
+    Caches: [NB, BS, Hkv, D] (same dtype as the input, or byte codes - fp8 e4m3fn, fp8 e5m2
+    or int8, named by cache_dtype "fp8" / "e5m2" / "i8" or by the tensor's dtype - with fp32
     meta [NB, BS, Hkv]) or [NB, BS, Hkv, 3*D/32] int32 3-bit words with fp16 meta
     [NB, BS, Hkv, 2]."""
     in_dt = _dtype16(k_new)

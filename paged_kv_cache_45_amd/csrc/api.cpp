@@ -31,7 +31,15 @@ int check_block_size(int bs) {
   return (bs == 16 || bs == 32 || bs == 64) ? PKV_OK : PKV_EUNSUPPORTED;
 }
 bool is16(pkv_dtype t) { return t == PKV_F16 || t == PKV_BF16; }
-bool known(pkv_dtype t) { return t == PKV_F16 || t == PKV_BF16 || t == PKV_FP8_E4M3FN || t == PKV_U3; }
+bool known(pkv_dtype t) {
+  return t == PKV_F16 || t == PKV_BF16 || t == PKV_FP8_E4M3FN || t == PKV_U3 || t == PKV_FP8_E5M2 ||
+         t == PKV_INT8;
+}
+// one byte code per element and one fp32 scale per row
+bool is_byte_code(pkv_dtype t) { return t == PKV_FP8_E4M3FN || t == PKV_FP8_E5M2 || t == PKV_INT8; }
+CacheKind byte_cache_kind(pkv_dtype t) {
+  return t == PKV_FP8_E5M2 ? CacheKind::E5m2 : t == PKV_INT8 ? CacheKind::I8 : CacheKind::Fp8;
+}
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -156,8 +164,8 @@ int kv_append(const void* k_new, const void* v_new, pkv_dtype in_dtype,
     return PKV_EINVAL;
   if (!aligned(slot_mapping, 8)) return PKV_EINVAL;
   CacheKind kind = CacheKind::Same;
-  if (cache_dtype == PKV_FP8_E4M3FN) {
-    kind = CacheKind::Fp8;
+  if (is_byte_code(cache_dtype)) {
+    kind = byte_cache_kind(cache_dtype);
     if (!aligned(k_cache, 8) || !aligned(v_cache, 8) || c_stride_block % 8 || c_stride_slot % 8 ||
         c_stride_head % 8)
       return PKV_EINVAL;
@@ -243,9 +251,9 @@ int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
     kind = CacheKind::U3;
     if (!aligned(k_cache, 4) || !aligned(v_cache, 4)) return PKV_EINVAL;
     if (!k_meta || !v_meta || !aligned(k_meta, 4) || !aligned(v_meta, 4)) return PKV_EINVAL;
-  } else if (cache_dtype == PKV_FP8_E4M3FN) {
+  } else if (is_byte_code(cache_dtype)) {
     // one lane reads 8 codes (8 bytes) of a row; one fp32 scale per (slot, kv head)
-    kind = CacheKind::Fp8;
+    kind = byte_cache_kind(cache_dtype);
     if (!aligned(k_cache, 8) || !aligned(v_cache, 8) || c_stride_block % 8 || c_stride_slot % 8 ||
         c_stride_head % 8)
       return PKV_EINVAL;
@@ -313,7 +321,7 @@ int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
   // decode gain ~10 %, 32 KB blocks of the Llama-8B step lose 15 %): at least 64 KB of K/V per
   // wave and block.  It also needs an even number of chunks per unit and at most 4 head waves.
   const int64_t row_bytes = cache_dtype == PKV_U3    ? 2 * (head_dim * 3 / 8 + 4)
-                            : cache_dtype == PKV_FP8_E4M3FN ? 2 * (int64_t)(head_dim + 4)
+                            : is_byte_code(cache_dtype) ? 2 * (int64_t)(head_dim + 4)
                                                             : 4 * (int64_t)head_dim;
   const int64_t wave_block_bytes = (int64_t)block_size * L.plan.hpi * row_bytes;
   const int unit_tokens = kClaimUnitChunks > 0 ? std::min(block_size, kClaimUnitChunks * L.plan.chunk_tokens)

@@ -4,7 +4,7 @@
 // slot < 0 marks padding and nothing of that token is loaded; block = slot / block_size,
 // offset = slot % block_size (shift and mask, block_size a power of two); K and V are
 // written by the same thread group; quantised caches divide by the scale in fp32 and
-// only then convert (fp8 arithmetic in fp8_quant.cuh).  The 3-bit cache follows
+// only then convert (fp8 e4m3fn, fp8 e5m2 and int8 arithmetic in fp8_quant.cuh).  The 3-bit cache follows
 // "triton-3bit-kv-cache-kernel" README, sections 1A/1B (bit layout) and section 2 test 3
 // (fp16 affine scale and zero).
 //
@@ -51,6 +51,32 @@ __device__ __forceinline__ void store_fp8_row(const uint4& x, uint8_t* dst, floa
   __builtin_nontemporal_store((u32x2_st){fp8_pack4(y[0], y[1], y[2], y[3]), fp8_pack4(y[4], y[5], y[6], y[7])},
                               reinterpret_cast<u32x2_st*>(dst));
   if (c == 0) *meta = q.s;
+}
+
+// e5m2 / int8 row: s = absmax / M (M = 57344 or 127; 1 for an all-zero row), y = clamp(x / s,
+// +-M) with the correctly rounded quotient, then the format's cast (fp8_quant.cuh).
+template <int LPR, bool BF16, CacheKind KIND>
+__device__ __forceinline__ void store_code_row(const uint4& x, uint8_t* dst, float* meta, int c) {
+  constexpr float M = KIND == CacheKind::E5m2 ? 57344.f : 127.f;
+  float f[8];
+  widen8<BF16>(x, f);
+  float a = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(f[e]));
+  a = group_max<LPR>(a);
+  const float s = (a == 0.f) ? 1.f : a / M;
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = fminf(fmaxf(f[e] / s, -M), M);
+  typedef uint32_t u32x2_st __attribute__((ext_vector_type(2)));
+  u32x2_st w;
+  if constexpr (KIND == CacheKind::E5m2) {
+    w = (u32x2_st){e5m2_pack4(y[0], y[1], y[2], y[3]), e5m2_pack4(y[4], y[5], y[6], y[7])};
+  } else {
+    w = (u32x2_st){i8_pack4(y[0], y[1], y[2], y[3]), i8_pack4(y[4], y[5], y[6], y[7])};
+  }
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x2_st*>(dst));
+  if (c == 0) *meta = s;
 }
 
 // u3 row: min/max affine parameters in fp32 rounded to fp16, codes clamp(rint(x/s + z), 0, 7),
@@ -142,6 +168,11 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
                                static_cast<float*>(p.k_meta) + mrow, c);
       store_fp8_row<LPR, BF16>(vx[k], static_cast<uint8_t*>(p.v_cache) + crow + c * 8,
                                static_cast<float*>(p.v_meta) + mrow, c);
+    } else if constexpr (byte_kind(KIND)) {
+      store_code_row<LPR, BF16, KIND>(kx[k], static_cast<uint8_t*>(p.k_cache) + crow + c * 8,
+                                      static_cast<float*>(p.k_meta) + mrow, c);
+      store_code_row<LPR, BF16, KIND>(vx[k], static_cast<uint8_t*>(p.v_cache) + crow + c * 8,
+                                      static_cast<float*>(p.v_meta) + mrow, c);
     } else {
       store_u3_row<LPR, BF16>(kx[k], static_cast<uint32_t*>(p.k_cache) + crow,
                               static_cast<uint32_t*>(p.k_meta) + mrow, c);
@@ -177,6 +208,8 @@ static hipError_t dispatch_kind(const AppendParams& p, CacheKind kind, hipStream
     case CacheKind::Same: return launch_append_t<D, BF16, CacheKind::Same>(p, s);
     case CacheKind::Fp8: return launch_append_t<D, BF16, CacheKind::Fp8>(p, s);
     case CacheKind::U3: return launch_append_t<D, BF16, CacheKind::U3>(p, s);
+    case CacheKind::E5m2: return launch_append_t<D, BF16, CacheKind::E5m2>(p, s);
+    case CacheKind::I8: return launch_append_t<D, BF16, CacheKind::I8>(p, s);
   }
   return hipErrorInvalidValue;
 }

@@ -102,6 +102,10 @@ const void* decode_kernel_ptr(int head_dim, int group, bool bf16, CacheKind kind
       return d128 ? decode_kernel_ptr_u3_d128(group, bf16, hpi, claim) : decode_kernel_ptr_u3_d64(group, bf16, hpi, claim);
     case CacheKind::Fp8:
       return d128 ? decode_kernel_ptr_fp8_d128(group, bf16, hpi, claim) : decode_kernel_ptr_fp8_d64(group, bf16, hpi, claim);
+    case CacheKind::E5m2:
+      return d128 ? decode_kernel_ptr_e5m2_d128(group, bf16, hpi, claim) : decode_kernel_ptr_e5m2_d64(group, bf16, hpi, claim);
+    case CacheKind::I8:
+      return d128 ? decode_kernel_ptr_i8_d128(group, bf16, hpi, claim) : decode_kernel_ptr_i8_d64(group, bf16, hpi, claim);
     default:
       return d128 ? decode_kernel_ptr_same_d128(group, bf16, hpi, claim) : decode_kernel_ptr_same_d64(group, bf16, hpi, claim);
   }
@@ -157,7 +161,7 @@ DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int head_di
                 (size_t)(P.token_streams - 1) * P.heads_per_group * group * (head_dim + 2) * sizeof(float);
   int per_cu = 0;
   for (int bf = 0; bf < 2; ++bf)
-    for (int kd = 0; kd < 3; ++kd) {                 // CacheKind values: Same, Fp8, U3
+    for (int kd = 0; kd < kNumCacheKinds; ++kd) {    // every CacheKind value
       if ((bf16 >= 0 && bf != bf16) || (kind >= 0 && kd != kind)) continue;
       const CacheKind ck = static_cast<CacheKind>(kd);
       per_cu = std::max(per_cu, resident_wgs_per_cu(decode_kernel_ptr(head_dim, group, bf != 0, ck, P.hpi, false),

@@ -8,9 +8,9 @@
 // accumulator).  GQA ("Write Triton Kv Cache Append Kernel", Kernel design rules): the G =
 // Hq / Hkv query heads h = kvh*G .. kvh*G+G-1 share kv head kvh.  The 3-bit cache
 // ("triton-3bit-kv-cache-kernel" README, title paragraph and section 2) is unpacked and
-// dequantised, x = (q - z) * s, in registers; the fp8 e4m3fn cache reads as decode(code) * s
-// with the row's scale (the inverse of the append's quantiser, "Write Triton Kv Cache Append
-// Kernel", Correctness requirements).  Split-K: the context of a (request, kv head)
+// dequantised, x = (q - z) * s, in registers; the byte-code caches (fp8 e4m3fn, fp8 e5m2,
+// int8) read as decode(code) * s with the row's scale (the inverse of the append's quantiser,
+// "Write Triton Kv Cache Append Kernel", Inputs item 4 and Correctness requirements).  Split-K: the context of a (request, kv head)
 // may be cut at multiples of the partition size into ranges that are reduced separately
 // and merged by log-sum-exp (the flash-decoding form the 3-bit README names).
 //
@@ -21,7 +21,7 @@
 //    heads of the same tokens at the same time, so whole slot rows are streamed and each
 //    opened DRAM page is used in full.  Lane layout: D/8 lanes per (head, token) row, each
 //    lane owning 8 consecutive elements (one 16-byte load of K and one of V; 8 bytes of
-//    codes for fp8).  The K/V stream is loaded with the non-temporal hint: it is read once.
+//    codes for the byte-code caches).  The K/V stream is loaded with the non-temporal hint: it is read once.
 //  * Work (stream-K): requests are cut into granules of `partition_size` tokens; the
 //    (request, head group, granule) units are laid end to end and the grid holds as many
 //    workgroups as the chip keeps resident, each taking a contiguous range of units sized
@@ -86,12 +86,26 @@ struct Geo {
   static_assert(RPI % HPI == 0 && 16 % CT == 0, "lane geometry");
 };
 
-template <int NI, CacheKind KIND> struct Regs;
-template <int NI> struct Regs<NI, CacheKind::Same> { uint4 k[NI], v[NI]; };
-template <int NI> struct Regs<NI, CacheKind::Fp8> {
-  uint2 k[NI], v[NI];                // 8 e4m3fn codes of the lane's row
+// byte-code caches (fp8 e4m3fn, fp8 e5m2, int8)
+// codes in bytes 2 HI and 2 HI + 1 of w -> a packed pair of 16-bit values, or two fp32 values
+template <CacheKind KIND, bool BF16, bool HI>
+__device__ __forceinline__ uint32_t codes2_to_16(uint32_t w) {
+  if constexpr (KIND == CacheKind::Fp8) return fp8x2_to_16<BF16, HI>(w);
+  else if constexpr (KIND == CacheKind::E5m2) return e5m2x2_to_16<BF16, HI>(w);
+  else return i8x2_to_16<BF16, HI>(w);
+}
+template <CacheKind KIND, bool HI>
+__device__ __forceinline__ void codes2_to_f32(uint32_t w, float& lo, float& hi) {
+  if constexpr (KIND == CacheKind::Fp8) fp8x2_to_f32<HI>(w, lo, hi);
+  else if constexpr (KIND == CacheKind::E5m2) e5m2x2_to_f32<HI>(w, lo, hi);
+  else i8x2_to_f32<HI>(w, lo, hi);
+}
+
+template <int NI, CacheKind KIND> struct Regs {
+  uint2 k[NI], v[NI];                // 8 codes of the lane's row
   float ks[NI], vs[NI];              // the row's scales
 };
+template <int NI> struct Regs<NI, CacheKind::Same> { uint4 k[NI], v[NI]; };
 template <int NI> struct Regs<NI, CacheKind::U3> {
   uint32_t klo[NI], khi[NI], vlo[NI], vhi[NI], km[NI], vm[NI];
 };
@@ -157,7 +171,7 @@ __device__ __forceinline__ LaneOffsets<D, HPI, KIND, G> lane_offsets(const Decod
                                                                    int c) {
   using Gm = Geo<D, HPI, G>;
   LaneOffsets<D, HPI, KIND, G> o;
-  constexpr int esz = KIND == CacheKind::U3 ? 4 : KIND == CacheKind::Fp8 ? 1 : 2;
+  constexpr int esz = KIND == CacheKind::U3 ? 4 : byte_kind(KIND) ? 1 : 2;
   const int col = KIND == CacheKind::U3 ? ((3 * c) >> 2) : c * 8;
 #pragma unroll
   for (int i = 0; i < Gm::NI; ++i) {
@@ -181,7 +195,7 @@ __device__ __forceinline__ void load_chunk(const char* kb, const char* vb, const
       R.k[i] = load_stream_u4(kb + o.row[i]);
       R.v[i] = load_stream_u4(vb + o.row[i]);
     }
-  } else if constexpr (KIND == CacheKind::Fp8) {
+  } else if constexpr (byte_kind(KIND)) {
 #pragma unroll
     for (int i = 0; i < Gm::NI; ++i) {
       R.k[i] = load_stream_u2(kb + o.row[i]);
@@ -217,19 +231,19 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
 #pragma unroll
   for (int i = 0; i < NI; ++i) valid[i] = !MASKED || (tok + i * Gm::TPI < t_end);
   float sc[NI][G];
-  if constexpr (KIND == CacheKind::Same || KIND == CacheKind::Fp8) {
+  if constexpr (KIND == CacheKind::Same || byte_kind(KIND)) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       uint32_t kw[4];
       if constexpr (KIND == CacheKind::Same) {
         kw[0] = R.k[i].x; kw[1] = R.k[i].y; kw[2] = R.k[i].z; kw[3] = R.k[i].w;
       } else {
-        // fp8: the 8 codes as exact 16-bit pairs of the query's type; the row scale multiplies
-        // the dot product: (s k) . q = s (k . q)
-        kw[0] = fp8x2_to_16<BF16, false>(R.k[i].x);
-        kw[1] = fp8x2_to_16<BF16, true>(R.k[i].x);
-        kw[2] = fp8x2_to_16<BF16, false>(R.k[i].y);
-        kw[3] = fp8x2_to_16<BF16, true>(R.k[i].y);
+        // byte codes: the 8 codes as exact 16-bit pairs of the query's type; the row scale
+        // multiplies the dot product: (s k) . q = s (k . q)
+        kw[0] = codes2_to_16<KIND, BF16, false>(R.k[i].x);
+        kw[1] = codes2_to_16<KIND, BF16, true>(R.k[i].x);
+        kw[2] = codes2_to_16<KIND, BF16, false>(R.k[i].y);
+        kw[3] = codes2_to_16<KIND, BF16, true>(R.k[i].y);
       }
       float d[G];
 #pragma unroll
@@ -242,7 +256,7 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
       // (with 8 heads: long-context decode +1 %)
       group_sum_n<LPR>(d);
       float scl = p.scale_log2;
-      if constexpr (KIND == CacheKind::Fp8) scl *= R.ks[i];
+      if constexpr (byte_kind(KIND)) scl *= R.ks[i];
 #pragma unroll
       for (int g = 0; g < G; ++g) sc[i][g] = valid[i] ? d[g] * scl : neg_inf();
     }
@@ -338,14 +352,14 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
         vf[2 * e + 1] = h_hi<BF16>(vw[e]);
       }
       pv_accumulate<G>(S, pp[i], 1.f, vf);
-    } else if constexpr (KIND == CacheKind::Fp8) {
+    } else if constexpr (byte_kind(KIND)) {
       uint32_t vw0 = R.v[i].x, vw1 = R.v[i].y;
       float vs = R.vs[i];
       if (MASKED && !valid[i]) { vw0 = vw1 = 0u; vs = 0.f; }          // poisoned tails stay out
-      fp8x2_to_f32<false>(vw0, vf[0], vf[1]);
-      fp8x2_to_f32<true>(vw0, vf[2], vf[3]);
-      fp8x2_to_f32<false>(vw1, vf[4], vf[5]);
-      fp8x2_to_f32<true>(vw1, vf[6], vf[7]);
+      codes2_to_f32<KIND, false>(vw0, vf[0], vf[1]);
+      codes2_to_f32<KIND, true>(vw0, vf[2], vf[3]);
+      codes2_to_f32<KIND, false>(vw1, vf[4], vf[5]);
+      codes2_to_f32<KIND, true>(vw1, vf[6], vf[7]);
       // sum_t p (s v_t) = sum_t (p s) v_t
       pv_accumulate<G>(S, pp[i], vs, vf);
     } else {
@@ -376,7 +390,7 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, State<G>& S, in
                                                  int t1, int lane, int tr, int hh, int c, int* cnt) {
   using Gm = Geo<D, HPI, G>;
   using R = Regs<Gm::NI, KIND>;
-  constexpr int esz = KIND == CacheKind::U3 ? 4 : KIND == CacheKind::Fp8 ? 1 : 2;
+  constexpr int esz = KIND == CacheKind::U3 ? 4 : byte_kind(KIND) ? 1 : 2;
   const int nk = (t1 - t0 + Gm::CT - 1) / Gm::CT;
   const bool ragged = ((t1 - t0) % Gm::CT) != 0;
   const int n_plain = ragged ? nk - 1 : nk;
@@ -455,7 +469,7 @@ __device__ __forceinline__ void run_claimed(const DecodeParams& p, State<G>& S, 
                                             int* claim, int lane, int tr, int hh, int c) {
   using Gm = Geo<D, HPI, G>;
   using R = Regs<Gm::NI, KIND>;
-  constexpr int esz = KIND == CacheKind::U3 ? 4 : KIND == CacheKind::Fp8 ? 1 : 2;
+  constexpr int esz = KIND == CacheKind::U3 ? 4 : byte_kind(KIND) ? 1 : 2;
   const int my_n = (1 << p.log2_claim) / Gm::CT;          // chunks per unit
   typedef const __attribute__((address_space(4))) int32_t* ConstIntPtr;
   const ConstIntPtr bt_row = (ConstIntPtr)(p.block_tables + b * p.bt_sb);
@@ -755,9 +769,9 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
 }
 
 // ---------------------------------------------------------------------------------------
-// Instance lookup.  The instances are compiled in six translation units (decode_{same, fp8,
-// u3}_d{128, 64}), each exporting the pointer lookup of its head dim and cache kind, so that
-// the build can compile them in parallel.
+// Instance lookup.  The instances are compiled in ten translation units (decode_{same, fp8,
+// e5m2, i8, u3}_d{128, 64}), each exporting the pointer lookup of its head dim and cache kind,
+// so that the build can compile them in parallel.
 // ---------------------------------------------------------------------------------------
 template <int D, int G, bool BF16, CacheKind KIND, int HPI>
 const void* kernel_ptr(bool claim) {
@@ -799,5 +813,9 @@ const void* decode_kernel_ptr_fp8_d128(int group, bool bf16, int hpi, bool claim
 const void* decode_kernel_ptr_fp8_d64(int group, bool bf16, int hpi, bool claim);
 const void* decode_kernel_ptr_u3_d128(int group, bool bf16, int hpi, bool claim);
 const void* decode_kernel_ptr_u3_d64(int group, bool bf16, int hpi, bool claim);
+const void* decode_kernel_ptr_e5m2_d128(int group, bool bf16, int hpi, bool claim);
+const void* decode_kernel_ptr_e5m2_d64(int group, bool bf16, int hpi, bool claim);
+const void* decode_kernel_ptr_i8_d128(int group, bool bf16, int hpi, bool claim);
+const void* decode_kernel_ptr_i8_d64(int group, bool bf16, int hpi, bool claim);
 
 }  // namespace pkv

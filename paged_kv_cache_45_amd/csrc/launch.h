@@ -6,7 +6,12 @@
 
 namespace pkv {
 
-enum class CacheKind : int { Same = 0, Fp8 = 1, U3 = 2 };
+enum class CacheKind : int { Same = 0, Fp8 = 1, U3 = 2, E5m2 = 3, I8 = 4 };
+constexpr int kNumCacheKinds = 5;
+// caches of one byte code per element with one fp32 scale per row: fp8 e4m3fn, fp8 e5m2, int8
+constexpr bool byte_kind(CacheKind k) {
+  return k == CacheKind::Fp8 || k == CacheKind::E5m2 || k == CacheKind::I8;
+}
 
 struct AppendParams {
   const void* k_new;
@@ -16,7 +21,7 @@ struct AppendParams {
   int64_t num_tokens;
   void* k_cache;
   void* v_cache;
-  int64_t c_sb, c_ss, c_sh;           // elements (bytes for fp8, words for u3)
+  int64_t c_sb, c_ss, c_sh;           // elements (bytes for byte codes, words for u3)
   void* k_meta;
   void* v_meta;
   int64_t capacity;                   // num_blocks * block_size

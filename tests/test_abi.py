@@ -61,6 +61,9 @@ def _append(lib, **kw):
     (dict(cdt=3), -1), (dict(nb=0), -1), (dict(H=0), -1), (dict(in_dtype=9), -1),
     (dict(T=(1 << 31) // 8), -2),
     (dict(ch=-128), -1),
+    (dict(cdt=4), -1), (dict(cdt=5), -1),                  # e5m2 / int8 without scale arrays
+    (dict(cdt=5, km=FAKE, vm=FAKE, cs=1028), -1),          # byte rows must stay 8-byte aligned
+    (dict(cdt=6), -1),                                     # no such dtype
 ])
 def test_append_validation(lib, kw, status):
     assert _append(lib, **kw) == status
@@ -88,6 +91,9 @@ def _decode(lib, **kw):
     (dict(B=9000, bts=257), -2),
     (dict(ws=None), -3), (dict(wsb=100), -3), (dict(scale=float("nan")), -1),
     (dict(q=FAKE8), -1), (dict(B=-1), -1), (dict(maxctx=-5), -1), (dict(cdt=3), -1),
+    (dict(cdt=4), -1), (dict(cdt=5), -1),                  # e5m2 / int8 without scale arrays
+    (dict(cdt=4, km=FAKE, vm=FAKE, ch=132), -1),           # byte rows must stay 8-byte aligned
+    (dict(cdt=6), -1),
 ])
 def test_decode_validation(lib, kw, status):
     assert _decode(lib, **kw) == status

@@ -17,6 +17,8 @@ from oracle import CacheSpec, append_ref
 
 pytestmark = pytest.mark.gpu
 
+BYTE_KINDS = ("fp8", "e5m2", "i8")       # fp8 e4m3fn, fp8 e5m2, int8: byte codes + fp32 row scales
+
 
 def _pools(kind, nb, bs, H, D, dtype, fill_seed=0):
     """Device pools pre-filled with random bits (so untouched bytes are checkable)."""
@@ -25,7 +27,7 @@ def _pools(kind, nb, bs, H, D, dtype, fill_seed=0):
         mk = lambda: torch.randint(-2**15, 2**15, (nb, bs, H, D), generator=g, device="cuda",
                                    dtype=torch.int32).to(torch.int16).view(dtype)
         return mk(), mk(), None, None
-    if kind == "fp8":
+    if kind in BYTE_KINDS:
         mk = lambda: torch.randint(0, 256, (nb, bs, H, D), generator=g, device="cuda",
                                    dtype=torch.int32).to(torch.uint8)
         mm = lambda: torch.rand((nb, bs, H), generator=g, device="cuda")
@@ -42,7 +44,7 @@ def _host(kind, t):
         return None
     if kind == "same":
         return bits16(t).copy()
-    if kind == "fp8":
+    if kind in BYTE_KINDS:
         return t.cpu().numpy().copy()
     return np_u32(t).copy()
 
@@ -90,7 +92,7 @@ def test_llama8b_decode_append_bf16():
                      wl.num_kv_heads, wl.head_dim)
 
 
-@pytest.mark.parametrize("kind", ["fp8", "same", "u3"])
+@pytest.mark.parametrize("kind", ["fp8", "same", "u3", "e5m2", "i8"])
 @pytest.mark.parametrize("qkv_view", [False, True])
 def test_mixed_append_full_size(kind, qkv_view):
     """Mixed prefill + decode append with 10% padding at full size (~11.5k tokens x 8 kv
@@ -103,7 +105,7 @@ def test_mixed_append_full_size(kind, qkv_view):
                      wl.num_kv_heads, wl.head_dim)
 
 
-@pytest.mark.parametrize("kind", ["same", "fp8", "u3"])
+@pytest.mark.parametrize("kind", ["same", "fp8", "u3", "e5m2", "i8"])
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 @pytest.mark.parametrize("D,bs", [(128, 16), (64, 32), (128, 64)])
 def test_append_kinds_small(kind, dtype, D, bs):
@@ -134,6 +136,30 @@ def test_fp8_every_16bit_input_value(dtype):
     slots = torch.arange(n_rows, dtype=torch.int64)
     nb = (n_rows + 15) // 16
     _run_and_compare(P, "fp8", k_new, v_new, slots, 16, nb, H, 128)
+
+
+@pytest.mark.parametrize("kind,top", [("e5m2", 57344.0), ("i8", 127.0)])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_byte_every_16bit_input_value(kind, top, dtype):
+    """Rows whose absmax is the format's top (57344 for e5m2, 127 for int8) have scale 1, so
+    y = x exactly: every fp16/bf16 value with |x| <= top goes through the cast once, both signs
+    (the int8 rows hold every tie k + 1/2 that the 16-bit formats can express)."""
+    P = need_gpu()
+    bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = torch.from_numpy(bits.view(np.int16)).view(dtype).float()
+    ok = torch.isfinite(vals) & (vals.abs() <= top)
+    xs = vals[ok]
+    per_row = 127
+    n_rows = (xs.numel() + per_row - 1) // per_row
+    pad = n_rows * per_row - xs.numel()
+    xs = torch.cat([xs, torch.zeros(pad)]).view(n_rows, per_row)
+    rows = torch.cat([torch.full((n_rows, 1), top), xs], dim=1).to(dtype)   # [R, 128]
+    print(f"{kind} {dtype}: {xs.numel() - pad} input values in {n_rows} rows", flush=True)
+    k_new = rows.view(n_rows, 1, 128).cuda()
+    v_new = (-rows).view(n_rows, 1, 128).cuda().contiguous()
+    slots = torch.arange(n_rows, dtype=torch.int64)
+    nb = (n_rows + 15) // 16
+    _run_and_compare(P, kind, k_new, v_new, slots, 16, nb, 1, 128)
 
 
 def test_u3_random_scales_bit_exact():
