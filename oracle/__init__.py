@@ -26,7 +26,7 @@ from .fp8 import (e4m3fn_decode_table, e4m3fn_encode_rne, e4m3fn_decode,
 from .quant3 import quantize_u3_rows, dequantize_u3_rows
 from .quant8 import (e5m2_decode_table, e5m2_decode, e5m2_encode_rne, quantize_e5m2_rows,
                      quantize_int8_rows, dequantize_e5m2_rows, dequantize_int8_rows, E5M2_MAX,
-                     INT8_MAX)
+                     INT8_MAX, quantize_given_scale, scale_offsets)
 from .slots import decode_slot_mapping, prefill_slot_mapping
 from .append import append_ref, CacheSpec
 from .attention import (paged_decode_ref, paged_decode_split_ref, lse_merge_ref,
@@ -38,6 +38,7 @@ __all__ = [
     "dequantize_fp8_rows", "E4M3_MAX", "quantize_u3_rows", "dequantize_u3_rows",
     "e5m2_decode_table", "e5m2_decode", "e5m2_encode_rne", "quantize_e5m2_rows",
     "quantize_int8_rows", "dequantize_e5m2_rows", "dequantize_int8_rows", "E5M2_MAX", "INT8_MAX",
+    "quantize_given_scale", "scale_offsets",
     "decode_slot_mapping", "prefill_slot_mapping", "append_ref", "CacheSpec",
     "paged_decode_ref", "paged_decode_split_ref", "lse_merge_ref", "gather_rows_f64", "PoolView",
 ]

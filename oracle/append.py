@@ -33,7 +33,7 @@ from typing import Optional
 import numpy as np
 
 from .fp8 import quantize_fp8_rows
-from .quant8 import quantize_e5m2_rows, quantize_int8_rows
+from .quant8 import quantize_e5m2_rows, quantize_int8_rows, quantize_given_scale, scale_offsets
 from .quant3 import quantize_u3_rows
 from .pack3 import pack_rows_u3
 
@@ -56,13 +56,18 @@ def to_f32(bits: np.ndarray, dtype: str) -> np.ndarray:
 
 def append_ref(k_new_bits: np.ndarray, v_new_bits: np.ndarray, slot_mapping: np.ndarray,
                k_cache: np.ndarray, v_cache: np.ndarray, spec: CacheSpec, block_size: int,
-               k_meta: Optional[np.ndarray] = None, v_meta: Optional[np.ndarray] = None) -> None:
+               k_meta: Optional[np.ndarray] = None, v_meta: Optional[np.ndarray] = None,
+               scale_strides=None) -> None:
     """Update the caches in place.
 
     k_new_bits, v_new_bits: uint16 [T, Hkv, D] (the raw fp16/bf16 bits).
     k_cache, v_cache: "same": uint16 [NB, BS, Hkv, D]; "fp8", "e5m2", "i8": uint8 [NB, BS, Hkv, D];
                       "u3": uint32 [NB, BS, Hkv, 3*D/32].
     k_meta, v_meta:   "fp8", "e5m2", "i8": float32 [NB, BS, Hkv]; "u3": float16 [NB, BS, Hkv, 2].
+    scale_strides:    byte-code caches only: None = the append computes and writes one scale
+                      per row (above); (sb, ss, sh) = k_meta / v_meta are the caller's scale
+                      arrays (any shape, read flat at block*sb + slot*ss + head*sh) and are
+                      only read (oracle/quant8.py, caller-given scales).
     """
     nb = k_cache.shape[0]
     T = slot_mapping.shape[0]
@@ -75,6 +80,10 @@ def append_ref(k_new_bits: np.ndarray, v_new_bits: np.ndarray, slot_mapping: np.
             row_bits = np.asarray(src[t])                 # [Hkv, D]
             if spec.kind == "same":
                 cache[blk, off] = row_bits
+            elif scale_strides is not None and spec.kind in ("fp8", "e5m2", "i8"):
+                heads = np.arange(row_bits.shape[0])
+                s = meta.reshape(-1)[scale_offsets(blk, off, heads, scale_strides)]
+                cache[blk, off] = quantize_given_scale(to_f32(row_bits, spec.in_dtype), s, spec.kind)
             elif spec.kind == "fp8":
                 codes, scale = quantize_fp8_rows(to_f32(row_bits, spec.in_dtype))
                 cache[blk, off] = codes

@@ -31,7 +31,7 @@ import numpy as np
 
 from .append import to_f32
 from .fp8 import dequantize_fp8_rows
-from .quant8 import dequantize_e5m2_rows, dequantize_int8_rows
+from .quant8 import dequantize_e5m2_rows, dequantize_int8_rows, scale_offsets
 from .pack3 import unpack_rows_u3
 from .quant3 import dequantize_u3_rows
 
@@ -40,22 +40,32 @@ class PoolView:
     """A cache pool as the oracle reads it: rows of (block, slot, kv head) -> float64."""
 
     def __init__(self, kind: str, cache: np.ndarray, meta=None, dtype: str = "bf16",
-                 head_dim: int = 0):
+                 head_dim: int = 0, scale_strides=None):
         self.kind, self.cache, self.meta, self.dtype = kind, cache, meta, dtype
+        # byte-code caches with caller-given scales: meta is read flat at
+        # block*sb + slot*ss + head*sh (oracle/quant8.py); None = one scale per row
+        self.scale_strides = scale_strides
         self.head_dim = head_dim if head_dim else (cache.shape[-1] if kind != "u3"
                                                    else cache.shape[-1] * 32 // 3)
 
     def rows(self, blocks: np.ndarray, kv_head: int) -> np.ndarray:
         """[n_blocks * BS, D] float64 rows of one kv head, in logical order."""
         c = self.cache[blocks, :, kv_head]                       # [nb, BS, ...]
+        if self.scale_strides is not None:
+            bs = self.cache.shape[1]
+            offs = scale_offsets(np.asarray(blocks)[:, None], np.arange(bs)[None, :], kv_head,
+                                 self.scale_strides)
+            scales = self.meta.reshape(-1)[offs]
+        elif self.kind in ("fp8", "e5m2", "i8"):
+            scales = self.meta[blocks, :, kv_head]
         if self.kind == "same":
             out = to_f32(c, self.dtype).astype(np.float64)
         elif self.kind == "fp8":
-            out = dequantize_fp8_rows(c, self.meta[blocks, :, kv_head])
+            out = dequantize_fp8_rows(c, scales)
         elif self.kind == "e5m2":
-            out = dequantize_e5m2_rows(c, self.meta[blocks, :, kv_head])
+            out = dequantize_e5m2_rows(c, scales)
         elif self.kind == "i8":
-            out = dequantize_int8_rows(c, self.meta[blocks, :, kv_head])
+            out = dequantize_int8_rows(c, scales)
         elif self.kind == "u3":
             q = unpack_rows_u3(c, self.head_dim)
             m = self.meta[blocks, :, kv_head]

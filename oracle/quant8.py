@@ -119,3 +119,42 @@ def dequantize_int8_rows(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
     """codes (int8, or their uint8 bytes) [..., D], scale [...] -> float64 code * s."""
     c = np.asarray(codes).view(np.int8) if np.asarray(codes).dtype == np.uint8 else np.asarray(codes)
     return c.astype(np.float64) * np.asarray(scale, dtype=np.float64)[..., None]
+
+
+# ---- caller-given scales ("Write Triton Kv Cache Append Kernel", Inputs items 4 and 8, step 6:
+# a per-tensor scale is divided out before the cast; per-token, per-head or per-block scales
+# are loaded first).  Reading: the caller owns the scale array; the scale of row
+# (block, slot, kv head) is scales[block * sb + slot * ss + head * sh], so that
+#   per-tensor        (sb, ss, sh) = (0, 0, 0)
+#   per-head          (0, 0, 1)
+#   per-block         (1, 0, 0)             one scale per physical block
+#   per-block-head    (num_kv_heads, 0, 1)
+#   per-token-head    (block_size * num_kv_heads, num_kv_heads, 1)   (the append's own layout)
+# Scales are positive and finite; the append reads them and never writes them.
+
+def scale_offsets(blocks: np.ndarray, slots: np.ndarray, heads: np.ndarray, strides) -> np.ndarray:
+    """Flat offsets of the scales of rows (block, slot, kv head) (broadcast), int64."""
+    sb, ss, sh = (int(v) for v in strides)
+    return (np.asarray(blocks, np.int64) * sb + np.asarray(slots, np.int64) * ss +
+            np.asarray(heads, np.int64) * sh)
+
+
+def quantize_given_scale(x: np.ndarray, s: np.ndarray, kind: str) -> np.ndarray:
+    """x: float32 [..., D], s: float32 [...] (the caller's scales) -> uint8 codes [..., D].
+
+    In float32: y_d = x_d / s (correctly rounded), clamped to the format's range (+-448 for
+    e4m3fn, +-57344 for e5m2, +-127 for int8), then the format's round-to-nearest-even cast.
+    """
+    from .fp8 import e4m3fn_encode_rne, E4M3_MAX
+    x = np.asarray(x, dtype=np.float32)
+    s = np.asarray(s, dtype=np.float32)
+    if np.any(~np.isfinite(s)) or np.any(s <= 0):
+        raise ValueError("scales must be positive and finite")
+    y = (x / s[..., None]).astype(np.float32)
+    if kind == "fp8":
+        return e4m3fn_encode_rne(np.clip(y, np.float32(-E4M3_MAX), np.float32(E4M3_MAX)))
+    if kind == "e5m2":
+        return e5m2_encode_rne(np.clip(y, np.float32(-E5M2_MAX), np.float32(E5M2_MAX)))
+    if kind == "i8":
+        return np.clip(np.rint(y), -INT8_MAX, INT8_MAX).astype(np.int8).view(np.uint8)
+    raise ValueError(kind)

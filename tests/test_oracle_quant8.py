@@ -148,3 +148,86 @@ def test_int8_round_trip_bound_and_symmetry():
 def test_e5m2_encoder_rejects_unclamped(bad):
     with pytest.raises(ValueError):
         e5m2_encode_rne(np.array([1.0, bad], np.float32))
+
+
+# ---- caller-given scales (per-tensor / per-head / per-block / per-token granularity)
+
+from oracle import (quantize_given_scale, scale_offsets, quantize_fp8_rows, append_ref, CacheSpec,
+                    PoolView)
+
+_ROW_QUANT = {"fp8": quantize_fp8_rows, "e5m2": quantize_e5m2_rows, "i8": quantize_int8_rows}
+
+
+@pytest.mark.parametrize("kind", ["fp8", "e5m2", "i8"])
+def test_given_scale_equal_to_row_scale_reduces_to_row_quantiser(kind):
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((50, 64)).astype(np.float32) * np.float32(2.5)
+    codes, s = _ROW_QUANT[kind](x)
+    assert np.array_equal(quantize_given_scale(x, s, kind), np.asarray(codes).view(np.uint8))
+
+
+def test_given_scale_worked_by_hand():
+    # s = 0.5: y = [2, -1.5, 600 (clamped), 0]
+    x = np.array([[1.0, -0.75, 300.0, 0.0]], np.float32)
+    s = np.array([0.5], np.float32)
+    # e4m3fn: 2 = 2^1 -> exponent field 8; -1.5 -> field 7, mantissa 4; 448 = 0x7E
+    assert quantize_given_scale(x, s, "fp8").tolist() == [[0x40, 0xBC, 0x7E, 0x00]]
+    # e5m2: 2 -> field 16; -1.5 -> field 15, mantissa 2; 600 clamps nowhere (< 57344) and
+    # rounds to 640 = 1.25 * 2^9 -> field 24, mantissa 1
+    assert quantize_given_scale(x, s, "e5m2").tolist() == [[0x40, 0xBE, 0x61, 0x00]]
+    # int8: -1.5 ties to -2; 600 saturates at 127
+    assert quantize_given_scale(x, s, "i8").view(np.int8).tolist() == [[2, -2, 127, 0]]
+    # e4m3fn saturation on the negative side
+    assert quantize_given_scale(np.array([[-1e6]], np.float32), s, "fp8").tolist() == [[0xFE]]
+
+
+@pytest.mark.parametrize("bad", [0.0, -1.0, np.inf, np.nan])
+def test_given_scale_rejects_bad_scales(bad):
+    with pytest.raises(ValueError):
+        quantize_given_scale(np.ones((1, 8), np.float32), np.array([bad], np.float32), "i8")
+
+
+@pytest.mark.parametrize("gran", ["tensor", "head", "block", "block_head", "token_head"])
+@pytest.mark.parametrize("kind", ["fp8", "e5m2", "i8"])
+def test_append_with_given_scales_reads_the_right_scale(gran, kind):
+    """Tiny pool, distinct scales per granule: every written row decodes within half a step of
+    its input under the scale its granule names, and the scale arrays are never written."""
+    NB, BS, H, D = 3, 4, 2, 8
+    strides = {"tensor": (0, 0, 0), "head": (0, 0, 1), "block": (1, 0, 0),
+               "block_head": (H, 0, 1), "token_head": (BS * H, H, 1)}[gran]
+    n_scales = {"tensor": 1, "head": H, "block": NB, "block_head": NB * H, "token_head": NB * BS * H}[gran]
+    rng = np.random.default_rng(9)
+    top = {"fp8": 448.0, "e5m2": 57344.0, "i8": 127.0}[kind]
+    # |x| < 3, so every y = x / s stays inside the format's range (saturation is pinned above)
+    scales = (rng.uniform(1.0, 2.0, n_scales) * 3.0 / top).astype(np.float32)
+    T = 7
+    x = rng.uniform(-3, 3, (T, H, D)).astype(np.float32)
+    bits = (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)     # bf16 (truncated)
+    slots = np.array([0, 5, -1, 11, 6, 3, 9], np.int64)
+    kc = np.zeros((NB, BS, H, D), np.uint8)
+    vc = kc.copy()
+    ks, vs = scales.copy(), scales.copy()
+    append_ref(bits, bits, slots, kc, vc, CacheSpec(kind, "bf16"), BS, ks, vs, scale_strides=strides)
+    assert np.array_equal(ks, scales) and np.array_equal(vs, scales)
+    pool = PoolView(kind, kc, ks, scale_strides=strides)
+    xb = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for t, slot in enumerate(slots):
+        if slot < 0:
+            continue
+        blk, off = divmod(int(slot), BS)
+        for h in range(H):
+            s = float(scales[scale_offsets(blk, off, h, strides)])
+            back = pool.rows(np.array([blk]), h)[off]
+            y = np.abs(xb[t, h] / s)
+            if kind == "i8":
+                step = np.full_like(y, 1.0)
+            else:
+                man = 3 if kind == "fp8" else 2
+                emin = -6 if kind == "fp8" else -14
+                step = 2.0 ** (np.floor(np.log2(np.maximum(y, 2.0 ** emin))) - man)
+            assert np.all(np.abs(back - xb[t, h]) <= step * s / 2 * (1 + 1e-6)), (gran, t, h)
+    # untouched slots stay zero
+    written = {int(v) for v in slots if v >= 0}
+    for slot in range(NB * BS):
+        if slot not in written:
+            assert not kc[divmod(slot, BS)].any()
