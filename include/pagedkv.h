@@ -114,6 +114,35 @@ int kv_append(const void* k_new, const void* v_new, pkv_dtype in_dtype,
               hipStream_t stream);
 
 /*
+ * kv_append_scaled - kv_append into a byte-code cache with scales the caller supplies.
+ *
+ * Defined by [Append], Inputs items 4 and 8 (fp8 / int8 caches with fp32 scales of per-tensor,
+ * per-token, per-head or per-block granularity, and their shape and indexing) and Required
+ * reasoning process step 6 (a per-tensor scale is divided out before the cast; per-token or
+ * per-block scales are loaded first).  Arguments as for kv_append, except:
+ *   cache_dtype      PKV_FP8_E4M3FN, PKV_FP8_E5M2 or PKV_INT8 (else PKV_EINVAL).
+ *   k_scale, v_scale device fp32, read only: the scale of row (blk, slot, h) is
+ *                    scale[blk*s_stride_block + slot*s_stride_slot + h*s_stride_head]
+ *                    (strides >= 0, in floats).  Per tensor: (0, 0, 0); per head: (0, 0, 1);
+ *                    per block: (1, 0, 0); per block and head: (num_kv_heads, 0, 1); per token
+ *                    and head: (block_size*num_kv_heads, num_kv_heads, 1).  Scales must be
+ *                    positive and finite (not checked: other values give undefined codes).
+ * Codes: y = clamp(x/s, +-M) with the correctly rounded fp32 quotient, M = 448, 57344 or 127,
+ * then RNE_e4m3fn(y), RNE_e5m2(y) or rint(y) (ties to even).  The scales are never written.
+ * Bit-exact by contract.
+ */
+int kv_append_scaled(const void* k_new, const void* v_new, pkv_dtype in_dtype,
+                     int64_t k_stride_tok, int64_t k_stride_head,
+                     int64_t v_stride_tok, int64_t v_stride_head,
+                     const int64_t* slot_mapping, int64_t num_tokens,
+                     void* k_cache, void* v_cache, pkv_dtype cache_dtype,
+                     int64_t c_stride_block, int64_t c_stride_slot, int64_t c_stride_head,
+                     const float* k_scale, const float* v_scale,
+                     int64_t s_stride_block, int64_t s_stride_slot, int64_t s_stride_head,
+                     int64_t num_blocks, int block_size, int num_kv_heads, int head_dim,
+                     hipStream_t stream);
+
+/*
  * paged_decode_workspace_size - bytes of workspace paged_decode needs.
  *
  * Split-K ("flash-decoding", named by [3bit] in its title paragraph as the form of its fused
@@ -182,6 +211,31 @@ int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
                  int batch, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                  int64_t num_blocks, int max_context_len, float sm_scale, int partition_size,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * paged_decode_scaled - paged_decode over a byte-code cache whose scales the caller supplies
+ * (the cache kv_append_scaled writes).
+ *
+ * Defined as paged_decode ([Paged], Step 1 and TODO 1-5), with each row read as decode(code) *
+ * s and s found as in kv_append_scaled ([Append], Inputs items 4 and 8: scale granularity and
+ * indexing).  Arguments as for paged_decode, except:
+ *   cache_dtype      PKV_FP8_E4M3FN, PKV_FP8_E5M2 or PKV_INT8 (else PKV_EINVAL).
+ *   k_scale, v_scale device fp32, read only, row (blk, slot, h) at blk*s_stride_block +
+ *                    slot*s_stride_slot + h*s_stride_head (strides >= 0, in floats;
+ *                    (16*s_stride_slot + num_kv_heads*s_stride_head)*4 < 2^31, else
+ *                    PKV_EUNSUPPORTED).
+ * The workspace is shared with paged_decode (same size query).
+ */
+int paged_decode_scaled(void* out, const void* q, pkv_dtype q_dtype,
+                        int64_t q_stride_b, int64_t q_stride_h, int64_t o_stride_b, int64_t o_stride_h,
+                        const void* k_cache, const void* v_cache, pkv_dtype cache_dtype,
+                        int64_t c_stride_block, int64_t c_stride_slot, int64_t c_stride_head,
+                        const float* k_scale, const float* v_scale,
+                        int64_t s_stride_block, int64_t s_stride_slot, int64_t s_stride_head,
+                        const int32_t* block_tables, int64_t bt_stride_b, const int32_t* context_lens,
+                        int batch, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                        int64_t num_blocks, int max_context_len, float sm_scale, int partition_size,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * pack3 / unpack3 - 3-bit packing, [3bit] sections 1A and 1B: value j of each group

@@ -7,8 +7,8 @@ in the HIP kernels.  There is no fallback: if the library is missing or a call f
 an exception is raised.
 
 Entry points (same names as the C ABI):
-    kv_append, paged_decode, paged_decode_workspace_size, pack3, unpack3,
-    pkv_status_string
+    kv_append, kv_append_scaled, paged_decode, paged_decode_scaled,
+    paged_decode_workspace_size, pack3, unpack3, pkv_status_string
 """
 from __future__ import annotations
 
@@ -17,7 +17,7 @@ import math
 import os
 from typing import Optional
 
-__all__ = ["kv_append", "paged_decode", "paged_decode_workspace_size", "pack3", "unpack3",
+__all__ = ["kv_append", "kv_append_scaled", "paged_decode", "paged_decode_scaled", "paged_decode_workspace_size", "pack3", "unpack3",
            "pkv_status_string", "decode_workspace", "library_path", "load_library",
            "PKV_F16", "PKV_BF16", "PKV_FP8_E4M3FN", "PKV_U3", "PKV_FP8_E5M2", "PKV_INT8",
            "PagedKVError"]
@@ -56,11 +56,18 @@ def load_library() -> ctypes.CDLL:
     lib.kv_append.restype = i32
     lib.kv_append.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, i64, vp, vp, i32, i64, i64, i64,
                               vp, vp, i64, i32, i32, i32, vp]
+    lib.kv_append_scaled.restype = i32
+    lib.kv_append_scaled.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, i64, vp, vp, i32, i64, i64,
+                                     i64, vp, vp, i64, i64, i64, i64, i32, i32, i32, vp]
     lib.paged_decode_workspace_size.restype = sz
     lib.paged_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.paged_decode.restype = i32
     lib.paged_decode.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, vp, i32, i64, i64, i64, vp, vp,
                                  vp, i64, vp, i32, i32, i32, i32, i32, i64, i32, f32, i32, vp, sz, vp]
+    lib.paged_decode_scaled.restype = i32
+    lib.paged_decode_scaled.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, vp, i32, i64, i64, i64,
+                                        vp, vp, i64, i64, i64, vp, i64, vp, i32, i32, i32, i32, i32,
+                                        i64, i32, f32, i32, vp, sz, vp]
     lib.pack3.restype = i32
     lib.pack3.argtypes = [vp, vp, i64, vp]
     lib.unpack3.restype = i32
@@ -127,20 +134,32 @@ def _cache_strides(k_cache, v_cache):
 
 
 def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_meta=None, v_meta=None,
-              cache_dtype=None, stream=None) -> None:
+              cache_dtype=None, stream=None, scale_strides=None) -> None:
     """Write new K/V [T, Hkv, D] into the paged pools through slot_mapping (int64 [T]).
 
     Caches: [NB, BS, Hkv, D] (same dtype as the input, or byte codes - fp8 e4m3fn, fp8 e5m2
     or int8, named by cache_dtype "fp8" / "e5m2" / "i8" or by the tensor's dtype - with fp32
     meta [NB, BS, Hkv]) or [NB, BS, Hkv, 3*D/32] int32 3-bit words with fp16 meta
-    [NB, BS, Hkv, 2]."""
+    [NB, BS, Hkv, 2].
+
+    scale_strides=(sb, ss, sh): byte-code caches with caller-given fp32 scales (kv_append_scaled):
+    k_meta / v_meta are then read, never written, at blk*sb + slot*ss + head*sh."""
     in_dt = _dtype16(k_new)
     if k_new.dim() != 3 or v_new.shape != k_new.shape or k_new.stride(2) != 1 or v_new.stride(2) != 1:
         raise ValueError("k_new / v_new must be [T, Hkv, D] with unit stride on D")
     cdt = _cache_dtype(k_cache, in_dt, cache_dtype)
     sb, ss, sh = _cache_strides(k_cache, v_cache)
     T, H, D = k_new.shape
-    st = load_library().kv_append(
+    lib = load_library()
+    if scale_strides is not None:
+        st = lib.kv_append_scaled(
+            _ptr(k_new), _ptr(v_new), in_dt, k_new.stride(0), k_new.stride(1), v_new.stride(0),
+            v_new.stride(1), _ptr(slot_mapping), T, _ptr(k_cache), _ptr(v_cache), cdt, sb, ss, sh,
+            _ptr(k_meta), _ptr(v_meta), *(int(v) for v in scale_strides), k_cache.shape[0],
+            k_cache.shape[1], H, D, _stream(stream))
+        _check("kv_append_scaled", st)
+        return
+    st = lib.kv_append(
         _ptr(k_new), _ptr(v_new), in_dt, k_new.stride(0), k_new.stride(1), v_new.stride(0),
         v_new.stride(1), _ptr(slot_mapping), T, _ptr(k_cache), _ptr(v_cache), cdt, sb, ss, sh,
         _ptr(k_meta), _ptr(v_meta), k_cache.shape[0], k_cache.shape[1], H, D, _stream(stream))
@@ -170,8 +189,11 @@ def decode_workspace(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: 
 def paged_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
                  sm_scale: Optional[float] = None, k_meta=None, v_meta=None, partition_size: int = 0,
                  workspace=None, out=None, cache_dtype=None, head_dim: Optional[int] = None,
-                 stream=None):
-    """Single-query paged attention: q [B, Hq, D] -> out [B, Hq, D] (q's dtype)."""
+                 stream=None, scale_strides=None):
+    """Single-query paged attention: q [B, Hq, D] -> out [B, Hq, D] (q's dtype).
+
+    scale_strides=(sb, ss, sh): byte-code caches with caller-given fp32 scales
+    (paged_decode_scaled), k_meta / v_meta read at blk*sb + slot*ss + head*sh."""
     import torch
     qdt = _dtype16(q)
     if q.dim() != 3 or q.stride(2) != 1:
@@ -189,14 +211,33 @@ def paged_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_le
         workspace = decode_workspace(B, Hq, k_cache.shape[2], D, max_context_len, partition_size,
                                      q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = load_library().paged_decode(
-        _ptr(out), _ptr(q), qdt, q.stride(0), q.stride(1), out.stride(0), out.stride(1),
-        _ptr(k_cache), _ptr(v_cache), cdt, sb, ss, sh, _ptr(k_meta), _ptr(v_meta),
-        _ptr(block_tables), block_tables.stride(0), _ptr(context_lens), B, Hq, k_cache.shape[2], D,
-        k_cache.shape[1], k_cache.shape[0], int(max_context_len), float(sm_scale),
-        int(partition_size), _ptr(workspace), wbytes, _stream(stream))
-    _check("paged_decode", st)
+    tail = (_ptr(block_tables), block_tables.stride(0), _ptr(context_lens), B, Hq, k_cache.shape[2], D,
+            k_cache.shape[1], k_cache.shape[0], int(max_context_len), float(sm_scale),
+            int(partition_size), _ptr(workspace), wbytes, _stream(stream))
+    head = (_ptr(out), _ptr(q), qdt, q.stride(0), q.stride(1), out.stride(0), out.stride(1),
+            _ptr(k_cache), _ptr(v_cache), cdt, sb, ss, sh, _ptr(k_meta), _ptr(v_meta))
+    if scale_strides is not None:
+        st = load_library().paged_decode_scaled(*head, *(int(v) for v in scale_strides), *tail)
+        _check("paged_decode_scaled", st)
+    else:
+        st = load_library().paged_decode(*head, *tail)
+        _check("paged_decode", st)
     return out
+
+
+def kv_append_scaled(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, scale_strides,
+                     cache_dtype=None, stream=None) -> None:
+    """kv_append into a byte-code cache with the caller's fp32 scales (read only), the scale of
+    row (blk, slot, head) at blk*sb + slot*ss + head*sh for scale_strides = (sb, ss, sh)."""
+    kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale, cache_dtype=cache_dtype,
+              stream=stream, scale_strides=scale_strides)
+
+
+def paged_decode_scaled(q, k_cache, v_cache, k_scale, v_scale, scale_strides, block_tables,
+                        context_lens, max_context_len: int, **kw):
+    """paged_decode over a byte-code cache with caller-given scales (see kv_append_scaled)."""
+    return paged_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+                        k_meta=k_scale, v_meta=v_scale, scale_strides=scale_strides, **kw)
 
 
 def pack3(values, packed=None, stream=None):

@@ -133,16 +133,20 @@ int unpack3(const uint8_t* packed, uint8_t* values, int64_t n_values, hipStream_
   return pkv::launch_unpack3(packed, values, n_values, stream) == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
-int kv_append(const void* k_new, const void* v_new, pkv_dtype in_dtype,
-              int64_t k_stride_tok, int64_t k_stride_head,
-              int64_t v_stride_tok, int64_t v_stride_head,
-              const int64_t* slot_mapping, int64_t num_tokens,
-              void* k_cache, void* v_cache, pkv_dtype cache_dtype,
-              int64_t c_stride_block, int64_t c_stride_slot, int64_t c_stride_head,
-              void* k_meta, void* v_meta,
-              int64_t num_blocks, int block_size, int num_kv_heads, int head_dim,
-              hipStream_t stream) {
+// kv_append and kv_append_scaled.  The meta entry (scale, or u3 scale/zero) of row (blk, slot,
+// head) is m_sb*blk + m_ss*slot + m_sh*head; given: the caller's scales are read, not written.
+static int append_impl(const void* k_new, const void* v_new, pkv_dtype in_dtype,
+                       int64_t k_stride_tok, int64_t k_stride_head,
+                       int64_t v_stride_tok, int64_t v_stride_head,
+                       const int64_t* slot_mapping, int64_t num_tokens,
+                       void* k_cache, void* v_cache, pkv_dtype cache_dtype,
+                       int64_t c_stride_block, int64_t c_stride_slot, int64_t c_stride_head,
+                       void* k_meta, void* v_meta,
+                       int64_t num_blocks, int block_size, int num_kv_heads, int head_dim,
+                       hipStream_t stream, int64_t m_sb, int64_t m_ss, int64_t m_sh, bool given) {
   if (!known(in_dtype) || !known(cache_dtype)) return PKV_EINVAL;
+  if (given && !is_byte_code(cache_dtype)) return PKV_EINVAL;
+  if (m_sb < 0 || m_ss < 0 || m_sh < 0) return PKV_EINVAL;
   if (!is16(in_dtype)) return PKV_EUNSUPPORTED;
   // a 16-bit cache must have the input's dtype (no implicit fp16 <-> bf16 conversion)
   if (is16(cache_dtype) && cache_dtype != in_dtype) return PKV_EINVAL;
@@ -195,11 +199,49 @@ int kv_append(const void* k_new, const void* v_new, pkv_dtype in_dtype,
   p.c_sh = c_stride_head;
   p.k_meta = k_meta;
   p.v_meta = v_meta;
+  p.m_sb = m_sb;
+  p.m_ss = m_ss;
+  p.m_sh = m_sh;
+  p.given_scale = given ? 1 : 0;
   p.capacity = num_blocks * block_size;
   p.log2_bs = log2_exact(block_size);
   p.num_kv_heads = num_kv_heads;
   const hipError_t e = pkv::launch_append(p, kind, in_dtype == PKV_BF16, head_dim, stream);
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+int kv_append(const void* k_new, const void* v_new, pkv_dtype in_dtype,
+              int64_t k_stride_tok, int64_t k_stride_head,
+              int64_t v_stride_tok, int64_t v_stride_head,
+              const int64_t* slot_mapping, int64_t num_tokens,
+              void* k_cache, void* v_cache, pkv_dtype cache_dtype,
+              int64_t c_stride_block, int64_t c_stride_slot, int64_t c_stride_head,
+              void* k_meta, void* v_meta,
+              int64_t num_blocks, int block_size, int num_kv_heads, int head_dim,
+              hipStream_t stream) {
+  // one meta entry per row, [num_blocks, block_size, num_kv_heads]
+  return append_impl(k_new, v_new, in_dtype, k_stride_tok, k_stride_head, v_stride_tok, v_stride_head,
+                     slot_mapping, num_tokens, k_cache, v_cache, cache_dtype, c_stride_block,
+                     c_stride_slot, c_stride_head, k_meta, v_meta, num_blocks, block_size,
+                     num_kv_heads, head_dim, stream, (int64_t)block_size * num_kv_heads, num_kv_heads,
+                     1, false);
+}
+
+int kv_append_scaled(const void* k_new, const void* v_new, pkv_dtype in_dtype,
+                     int64_t k_stride_tok, int64_t k_stride_head,
+                     int64_t v_stride_tok, int64_t v_stride_head,
+                     const int64_t* slot_mapping, int64_t num_tokens,
+                     void* k_cache, void* v_cache, pkv_dtype cache_dtype,
+                     int64_t c_stride_block, int64_t c_stride_slot, int64_t c_stride_head,
+                     const float* k_scale, const float* v_scale,
+                     int64_t s_stride_block, int64_t s_stride_slot, int64_t s_stride_head,
+                     int64_t num_blocks, int block_size, int num_kv_heads, int head_dim,
+                     hipStream_t stream) {
+  return append_impl(k_new, v_new, in_dtype, k_stride_tok, k_stride_head, v_stride_tok, v_stride_head,
+                     slot_mapping, num_tokens, k_cache, v_cache, cache_dtype, c_stride_block,
+                     c_stride_slot, c_stride_head, const_cast<float*>(k_scale),
+                     const_cast<float*>(v_scale), num_blocks, block_size, num_kv_heads, head_dim,
+                     stream, s_stride_block, s_stride_slot, s_stride_head, true);
 }
 
 size_t paged_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int head_dim,
@@ -214,16 +256,19 @@ size_t paged_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads,
   return decode_layout(batch, num_q_heads, num_kv_heads, head_dim, max_context_len, ps, -1, -1).bytes;
 }
 
-int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
-                 int64_t q_stride_b, int64_t q_stride_h, int64_t o_stride_b, int64_t o_stride_h,
-                 const void* k_cache, const void* v_cache, pkv_dtype cache_dtype,
-                 int64_t c_stride_block, int64_t c_stride_slot, int64_t c_stride_head,
-                 const void* k_meta, const void* v_meta,
-                 const int32_t* block_tables, int64_t bt_stride_b, const int32_t* context_lens,
-                 int batch, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                 int64_t num_blocks, int max_context_len, float sm_scale, int partition_size,
-                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// paged_decode and paged_decode_scaled; meta entry of row (blk, slot, head) as for append_impl.
+static int decode_impl(void* out, const void* q, pkv_dtype q_dtype,
+                       int64_t q_stride_b, int64_t q_stride_h, int64_t o_stride_b, int64_t o_stride_h,
+                       const void* k_cache, const void* v_cache, pkv_dtype cache_dtype,
+                       int64_t c_stride_block, int64_t c_stride_slot, int64_t c_stride_head,
+                       const void* k_meta, const void* v_meta,
+                       const int32_t* block_tables, int64_t bt_stride_b, const int32_t* context_lens,
+                       int batch, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                       int64_t num_blocks, int max_context_len, float sm_scale, int partition_size,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream,
+                       int64_t m_sb, int64_t m_ss, int64_t m_sh) {
   if (!known(q_dtype) || !known(cache_dtype)) return PKV_EINVAL;
+  if (m_sb < 0 || m_ss < 0 || m_sh < 0) return PKV_EINVAL;
   if (!is16(q_dtype)) return PKV_EUNSUPPORTED;
   if (is16(cache_dtype) && cache_dtype != q_dtype) return PKV_EINVAL;
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_context_len < 0)
@@ -265,7 +310,8 @@ int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
   }
   if (!aligned(block_tables, 4) || !aligned(context_lens, 4)) return PKV_EINVAL;
   // per-lane row offsets inside a 16-slot chunk are 32-bit byte offsets
-  if ((c_stride_slot * 16 + c_stride_head * (int64_t)num_kv_heads) * 4 >= 0x7fffffffLL)
+  if ((c_stride_slot * 16 + c_stride_head * (int64_t)num_kv_heads) * 4 >= 0x7fffffffLL ||
+      (m_ss * 16 + m_sh * (int64_t)num_kv_heads) * 4 >= 0x7fffffffLL)
     return PKV_EUNSUPPORTED;
   if (bt_stride_b < cdiv(max_context_len, block_size)) return PKV_EINVAL;
   const int ps = resolve_partition(partition_size, max_context_len, batch, num_q_heads);
@@ -290,6 +336,9 @@ int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
   p.c_sh = c_stride_head;
   p.k_meta = k_meta;
   p.v_meta = v_meta;
+  p.m_sb = m_sb;
+  p.m_ss = m_ss;
+  p.m_sh = m_sh;
   p.block_tables = block_tables;
   p.bt_sb = bt_stride_b;
   p.context_lens = context_lens;
@@ -338,6 +387,42 @@ int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
   p.split_w[3] = sw.rest_odd;
   const hipError_t e = pkv::launch_decode(p, L.plan, kind, q_dtype == PKV_BF16, head_dim, group, stream);
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
+                 int64_t q_stride_b, int64_t q_stride_h, int64_t o_stride_b, int64_t o_stride_h,
+                 const void* k_cache, const void* v_cache, pkv_dtype cache_dtype,
+                 int64_t c_stride_block, int64_t c_stride_slot, int64_t c_stride_head,
+                 const void* k_meta, const void* v_meta,
+                 const int32_t* block_tables, int64_t bt_stride_b, const int32_t* context_lens,
+                 int batch, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                 int64_t num_blocks, int max_context_len, float sm_scale, int partition_size,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  // one meta entry per row, [num_blocks, block_size, num_kv_heads]
+  return decode_impl(out, q, q_dtype, q_stride_b, q_stride_h, o_stride_b, o_stride_h, k_cache, v_cache,
+                     cache_dtype, c_stride_block, c_stride_slot, c_stride_head, k_meta, v_meta,
+                     block_tables, bt_stride_b, context_lens, batch, num_q_heads, num_kv_heads,
+                     head_dim, block_size, num_blocks, max_context_len, sm_scale, partition_size,
+                     workspace, workspace_bytes, stream, (int64_t)block_size * num_kv_heads,
+                     num_kv_heads, 1);
+}
+
+int paged_decode_scaled(void* out, const void* q, pkv_dtype q_dtype,
+                        int64_t q_stride_b, int64_t q_stride_h, int64_t o_stride_b, int64_t o_stride_h,
+                        const void* k_cache, const void* v_cache, pkv_dtype cache_dtype,
+                        int64_t c_stride_block, int64_t c_stride_slot, int64_t c_stride_head,
+                        const float* k_scale, const float* v_scale,
+                        int64_t s_stride_block, int64_t s_stride_slot, int64_t s_stride_head,
+                        const int32_t* block_tables, int64_t bt_stride_b, const int32_t* context_lens,
+                        int batch, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                        int64_t num_blocks, int max_context_len, float sm_scale, int partition_size,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!is_byte_code(cache_dtype)) return PKV_EINVAL;
+  return decode_impl(out, q, q_dtype, q_stride_b, q_stride_h, o_stride_b, o_stride_h, k_cache, v_cache,
+                     cache_dtype, c_stride_block, c_stride_slot, c_stride_head, k_scale, v_scale,
+                     block_tables, bt_stride_b, context_lens, batch, num_q_heads, num_kv_heads,
+                     head_dim, block_size, num_blocks, max_context_len, sm_scale, partition_size,
+                     workspace, workspace_bytes, stream, s_stride_block, s_stride_slot, s_stride_head);
 }
 
 }  // extern "C"

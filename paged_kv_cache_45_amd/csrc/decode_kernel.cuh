@@ -177,7 +177,7 @@ __device__ __forceinline__ LaneOffsets<D, HPI, KIND, G> lane_offsets(const Decod
   for (int i = 0; i < Gm::NI; ++i) {
     const int64_t slot = tr + i * Gm::TPI;
     o.row[i] = (uint32_t)((slot * p.c_ss + (int64_t)hh * p.c_sh + col) * esz);
-    o.meta[i] = (uint32_t)((slot * p.num_kv_heads + hh) * 4);
+    o.meta[i] = (uint32_t)((slot * p.m_ss + (int64_t)hh * p.m_sh) * 4);
   }
   return o;
 }
@@ -399,8 +399,8 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, State<G>& S, in
   const LaneOffsets<D, HPI, KIND, G> lo = lane_offsets<D, HPI, KIND, G>(p, tr, hh, c);
   const char* kc = static_cast<const char*>(p.k_cache) + (int64_t)h_first * p.c_sh * esz;
   const char* vc = static_cast<const char*>(p.v_cache) + (int64_t)h_first * p.c_sh * esz;
-  const char* kmc = static_cast<const char*>(p.k_meta) + (int64_t)h_first * 4;
-  const char* vmc = static_cast<const char*>(p.v_meta) + (int64_t)h_first * 4;
+  const char* kmc = static_cast<const char*>(p.k_meta) + (int64_t)h_first * p.m_sh * 4;
+  const char* vmc = static_cast<const char*>(p.v_meta) + (int64_t)h_first * p.m_sh * 4;
   typedef __attribute__((address_space(3))) int LdsInt;
   LdsInt* const cnt_lds = (LdsInt*)cnt;                   // an LDS atomic (ds_add_rtn, lgkmcnt)
   auto claim = [&]() {
@@ -426,7 +426,7 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, State<G>& S, in
     const int64_t phys = __builtin_amdgcn_readlane(bt_lane, k - win);
     const int64_t slot0 = tok0 & (p.block_size - 1);
     const int64_t rowb = (phys * p.c_sb + slot0 * p.c_ss) * esz;
-    const int64_t metab = ((phys * p.block_size + slot0) * p.num_kv_heads) * 4;
+    const int64_t metab = (phys * p.m_sb + slot0 * p.m_ss) * 4;
     load_chunk<D, HPI, KIND, G>(kc + rowb, vc + rowb, kmc + metab, vmc + metab, lo, c, regs);
   };
   auto tok_of = [&](int k) { return t0 + k * Gm::CT + tr; };
@@ -477,8 +477,8 @@ __device__ __forceinline__ void run_claimed(const DecodeParams& p, State<G>& S, 
   const LaneOffsets<D, HPI, KIND, G> lo = lane_offsets<D, HPI, KIND, G>(p, tr, hh, c);
   const char* kc = static_cast<const char*>(p.k_cache) + (int64_t)h_first * p.c_sh * esz;
   const char* vc = static_cast<const char*>(p.v_cache) + (int64_t)h_first * p.c_sh * esz;
-  const char* kmc = static_cast<const char*>(p.k_meta) + (int64_t)h_first * 4;
-  const char* vmc = static_cast<const char*>(p.v_meta) + (int64_t)h_first * 4;
+  const char* kmc = static_cast<const char*>(p.k_meta) + (int64_t)h_first * p.m_sh * 4;
+  const char* vmc = static_cast<const char*>(p.v_meta) + (int64_t)h_first * p.m_sh * 4;
   // a claim outside [0, nu) ends the loop: a counter that is not zero at the start of the call
   // (a workspace that was not zero-filled) can only lose work, never read outside the segment
   auto take = [&](int v) { return (unsigned)v < (unsigned)nu ? v : nu; };
@@ -503,7 +503,7 @@ __device__ __forceinline__ void run_claimed(const DecodeParams& p, State<G>& S, 
   auto issue = [&](const Loc& l, int k, R& regs) {         // chunk k (tokens k * CT) of a unit
     const int64_t slot0 = l.slot + k * Gm::CT;
     const int64_t rowb = (l.phys * p.c_sb + slot0 * p.c_ss) * esz;
-    const int64_t metab = ((l.phys * p.block_size + slot0) * p.num_kv_heads) * 4;
+    const int64_t metab = (l.phys * p.m_sb + slot0 * p.m_ss) * 4;
     load_chunk<D, HPI, KIND, G>(kc + rowb, vc + rowb, kmc + metab, vmc + metab, lo, c, regs);
   };
   int uc = take(__builtin_amdgcn_readfirstlane(claim_async()));

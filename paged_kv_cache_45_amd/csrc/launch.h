@@ -24,6 +24,8 @@ struct AppendParams {
   int64_t c_sb, c_ss, c_sh;           // elements (bytes for byte codes, words for u3)
   void* k_meta;
   void* v_meta;
+  int64_t m_sb, m_ss, m_sh;           // meta entry of row (blk, slot, head): blk*m_sb + slot*m_ss + head*m_sh
+  int given_scale;                    // byte codes: 1 = read the caller's scales, 0 = compute and write
   int64_t capacity;                   // num_blocks * block_size
   int log2_bs;
   int num_kv_heads;
@@ -36,8 +38,9 @@ struct DecodeParams {
   const void* k_cache;
   const void* v_cache;
   int64_t c_sb, c_ss, c_sh;           // elements (words for u3)
-  const void* k_meta;                 // u3: fp16 (s, z) per row, contiguous [NB, BS, Hkv]
+  const void* k_meta;                 // u3: fp16 (s, z) per row; byte codes: fp32 scales
   const void* v_meta;
+  int64_t m_sb, m_ss, m_sh;           // meta entry of row (blk, slot, head): blk*m_sb + slot*m_ss + head*m_sh
   const int32_t* block_tables;
   int64_t bt_sb;
   const int32_t* context_lens;

@@ -28,7 +28,7 @@ def lib():
 def test_header_declares_the_four_calls():
     names = _declared_functions()
     for n in ("kv_append", "paged_decode", "paged_decode_workspace_size", "pack3", "unpack3",
-              "pkv_status_string"):
+              "pkv_status_string", "kv_append_scaled", "paged_decode_scaled"):
         assert n in names, names
 
 
@@ -129,3 +129,38 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(P, "library_path", lambda: str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError):
         P.load_library()
+
+
+def _append_scaled(lib, **kw):
+    a = dict(k_new=FAKE, v_new=FAKE, in_dtype=1, ks_t=1024, ks_h=128, vs_t=1024, vs_h=128,
+             slots=FAKE, T=4, kc=FAKE, vc=FAKE, cdt=2, cb=16384, cs=1024, ch=128, ks=FAKE, vs=FAKE,
+             ssb=0, sss=0, ssh=0, nb=8, bs=16, H=8, D=128, stream=None)
+    a.update(kw)
+    return lib.kv_append_scaled(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cdt=1), -1), (dict(cdt=3), -1),                  # not a byte-code cache
+    (dict(ks=None), -1), (dict(ssh=-1), -1), (dict(sss=-8), -1), (dict(cdt=9), -1),
+    (dict(T=0), 0),
+])
+def test_append_scaled_validation(lib, kw, status):
+    assert _append_scaled(lib, **kw) == status
+
+
+def _decode_scaled(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, qdt=1, qsb=4096, qsh=128, osb=4096, osh=128, kc=FAKE, vc=FAKE, cdt=5,
+             cb=16384, cs=1024, ch=128, ks=FAKE, vs=FAKE, ssb=1, sss=0, ssh=0, bt=FAKE, bts=257,
+             ctx=FAKE, B=64, Hq=32, Hkv=8, D=128, bs=16, nb=1000, maxctx=4097, scale=0.088, ps=0,
+             ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.paged_decode_scaled(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cdt=1), -1), (dict(cdt=3), -1), (dict(vs=None), -1), (dict(ssb=-1), -1),
+    (dict(sss=1 << 26), -2),                               # lane scale offsets beyond 32 bits
+    (dict(B=0), 0), (dict(ws=None), -3),
+])
+def test_decode_scaled_validation(lib, kw, status):
+    assert _decode_scaled(lib, **kw) == status

@@ -135,3 +135,99 @@ def test_byte_decode_block_claiming_ragged(kind):
                              max(lens), wl.sm_scale, k_meta=gpu[2], v_meta=gpu[3], workspace=ws,
                              cache_dtype=kind)
         assert report(f"{kind} claims rep{rep}", f32_of(out), want, wl.dtype) <= ATTN_TOL
+
+
+# ---- caller-given scales (kv_append_scaled / paged_decode_scaled): "Write Triton Kv Cache
+# Append Kernel", Inputs items 4 and 8 (per-tensor, per-token, per-head or per-block scales)
+# and step 6 (load the scale, divide in fp32, cast).
+
+from oracle import append_ref, CacheSpec, quantize_given_scale, scale_offsets
+from gpu_helpers import bits16, dtype_name
+
+TOPS = {"fp8": 448.0, "e5m2": 57344.0, "i8": 127.0}
+
+
+def _granularity(gran, NB, BS, H):
+    """(scale strides, number of scales) of a granularity."""
+    return {"tensor": ((0, 0, 0), 1), "head": ((0, 0, 1), H), "block": ((1, 0, 0), NB),
+            "block_head": ((H, 0, 1), NB * H), "token_head": ((BS * H, H, 1), NB * BS * H)}[gran]
+
+
+def _given_scale_case(P, wl, kind, gran, seed, blocks=None):
+    """Quantise every slot of wl's pools with kv_append_scaled; returns the GPU pools, the
+    scales and the oracle's pools, after checking the pools bit for bit (all slots through the
+    oracle's append, or only `blocks`, quantised by the oracle's row quantiser directly)."""
+    NB, BS, H, D = wl.k_pool.shape
+    strides, n = _granularity(gran, NB, BS, H)
+    rng = np.random.default_rng(seed)
+    amax = float(max(wl.k_pool.abs().max(), wl.v_pool.abs().max()))
+    # scales around the pool's absmax / top: most rows in range, the largest ones saturate
+    ks = (rng.uniform(0.6, 1.4, n) * amax / TOPS[kind]).astype(np.float32)
+    vs = (rng.uniform(0.6, 1.4, n) * amax / TOPS[kind]).astype(np.float32)
+    kc = torch.empty((NB, BS, H, D), dtype=torch.uint8, device="cuda")
+    vc = torch.empty_like(kc)
+    ks_d, vs_d = torch.from_numpy(ks).cuda(), torch.from_numpy(vs).cuda()
+    slots = torch.arange(NB * BS, dtype=torch.int64)
+    P.kv_append_scaled(wl.k_pool.reshape(NB * BS, H, D), wl.v_pool.reshape(NB * BS, H, D),
+                       slots.cuda(), kc, vc, ks_d, vs_d, strides, cache_dtype=kind)
+    torch.cuda.synchronize()
+    assert np.array_equal(ks_d.cpu().numpy(), ks) and np.array_equal(vs_d.cpu().numpy(), vs)
+    hk = np.zeros((NB, BS, H, D), np.uint8)
+    hv = hk.copy()
+    if blocks is None:
+        append_ref(bits16(wl.k_pool.reshape(NB * BS, H, D)), bits16(wl.v_pool.reshape(NB * BS, H, D)),
+                   slots.numpy(), hk, hv, CacheSpec(kind, dtype_name(wl.dtype)), BS, ks.copy(),
+                   vs.copy(), scale_strides=strides)
+        assert np.array_equal(kc.cpu().numpy(), hk), "K pool differs"
+        assert np.array_equal(vc.cpu().numpy(), hv), "V pool differs"
+    else:
+        blk = np.array(sorted(blocks), np.int64)
+        offs = scale_offsets(blk[:, None, None], np.arange(BS)[None, :, None], np.arange(H)[None, None, :],
+                             strides)
+        for pool, sc, host, dev in ((wl.k_pool, ks, hk, kc), (wl.v_pool, vs, hv, vc)):
+            host[blk] = quantize_given_scale(f32_of(pool[blk]), sc[offs], kind)
+            assert np.array_equal(dev[blk].cpu().numpy(), host[blk])
+    kpool = PoolView(kind, hk, ks, scale_strides=strides)
+    vpool = PoolView(kind, hv, vs, scale_strides=strides)
+    return (kc, vc, ks_d, vs_d), strides, kpool, vpool
+
+
+@pytest.mark.parametrize("kind", ["fp8", "e5m2", "i8"])
+@pytest.mark.parametrize("gran", ["tensor", "head", "block", "block_head", "token_head"])
+def test_given_scales_append_and_decode_ragged(kind, gran):
+    P = need_gpu()
+    lens = [1, 15, 16, 17, 511, 512, 513, 1000, 0, 33]
+    wl = W.decode_workload(f"{kind}-{gran}", batch=len(lens), num_q_heads=8, num_kv_heads=2,
+                           head_dim=128, block_size=16, ctx_lo=0, ctx_hi=0, dtype=torch.bfloat16,
+                           device="cuda", seed=500 + len(gran), append_one=False, ctx_override=lens,
+                           poison=False)
+    gpu, strides, kpool, vpool = _given_scale_case(P, wl, kind, gran, seed=len(gran) + len(kind))
+    want = paged_decode_ref(f32_of(wl.q), kpool, vpool, wl.block_tables.numpy(), np.array(lens),
+                            wl.block_size, wl.num_kv_heads, wl.sm_scale)
+    for ps in (0, 512):
+        out = P.paged_decode_scaled(wl.q, gpu[0], gpu[1], gpu[2], gpu[3], strides,
+                                    wl.block_tables.cuda(), wl.ctx_after.cuda(), max(lens),
+                                    sm_scale=wl.sm_scale, partition_size=ps, cache_dtype=kind)
+        got = f32_of(out)
+        assert np.all(got[lens.index(0)] == 0)
+        assert report(f"{kind} {gran} ps{ps}", got, want, wl.dtype) <= ATTN_TOL
+
+
+def test_given_per_tensor_fp8_llama8b_full_size_sampled():
+    """Per-tensor fp8 e4m3fn scales at the Llama-8B decode shape (B=64, 32/8 heads, D=128,
+    BS 16, U{512..4096}), the whole pool quantised by kv_append_scaled and checked bit for bit;
+    decode checked on 3 requests."""
+    P = need_gpu()
+    wl = W.llama8b_decode("cuda", poison=False)
+    sample_b = (0, 29, 63)
+    blocks = {blk for b in sample_b for blk in wl.blocks_of[b]}
+    gpu, strides, kpool, vpool = _given_scale_case(P, wl, "fp8", "tensor", seed=3, blocks=blocks)
+    ctx = wl.ctx_before.numpy()
+    out = P.paged_decode_scaled(wl.q, gpu[0], gpu[1], gpu[2], gpu[3], strides, wl.block_tables.cuda(),
+                                wl.ctx_before.cuda(), int(ctx.max()), sm_scale=wl.sm_scale,
+                                cache_dtype="fp8")
+    heads = [(b, h) for b in sample_b for h in range(wl.num_q_heads)]
+    want = paged_decode_ref(f32_of(wl.q), kpool, vpool, wl.block_tables.numpy(), ctx,
+                            wl.block_size, wl.num_kv_heads, wl.sm_scale, heads=heads)
+    sel = np.array([b for b, _ in heads]), np.array([h for _, h in heads])
+    assert report("fp8 per-tensor llama8b", f32_of(out)[sel], want[sel], wl.dtype) <= ATTN_TOL
