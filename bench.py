@@ -25,6 +25,7 @@ of the remaining shapes:
   fp8-decode         the Llama-8B decode shape over fp8 e4m3fn pools with per-row fp32 scales
   e5m2-decode        the same over fp8 e5m2 pools
   int8-decode        the same over int8 pools
+  fp8-tensor-scale-decode  the fp8 e4m3fn pools with one caller-given scale per pool
                      (KV GB/s; the pools hold half the bytes of the bf16 ones)
   dual-stacked-decode  the Llama-8B decode shape over the dual-stacked block layout
                      [num_blocks, 2, num_kv_heads, block_size, head_dim], as strided views (KV GB/s)
@@ -437,25 +438,34 @@ def run_packed3(args, P, W):
 
 BYTE_CACHES = {"fp8": ("fp8-decode", "fp8 e4m3fn"), "e5m2": ("e5m2-decode", "fp8 e5m2"),
                "i8": ("int8-decode", "int8")}
+TOP = {"fp8": 448.0, "e5m2": 57344.0, "i8": 127.0}
 
 
-def run_fp8_decode(args, P, W, kind="fp8"):
+def run_fp8_decode(args, P, W, kind="fp8", per_tensor=False):
     """paged_decode at the Llama-8B shape over byte-code pools (fp8 e4m3fn, fp8 e5m2 or int8,
     one fp32 scale per row), quantised from four bf16 layer pools through kv_append and read in
-    rotation."""
+    rotation.  per_tensor: one caller-given scale per pool (kv_append_scaled /
+    paged_decode_scaled) instead of one scale per row."""
     import torch
     name, label = BYTE_CACHES[kind]
+    if per_tensor:
+        name = name.replace("-decode", "-tensor-scale-decode")
+    strides = (0, 0, 0) if per_tensor else None
     pools = []
     for i in range(N_LAYERS):
         wl = W.llama8b_decode("cuda", data_seed=W.BASE_SEED + 2 + 1000 * i, poison=False)
         NB, BS, H, D = wl.k_pool.shape
         kc = torch.empty((NB, BS, H, D), dtype=torch.uint8, device="cuda")
         vc = torch.empty_like(kc)
-        km = torch.empty((NB, BS, H), dtype=torch.float32, device="cuda")
-        vm = torch.empty_like(km)
+        if per_tensor:
+            km = (wl.k_pool.abs().max().float() / TOP[kind]).reshape(1)
+            vm = (wl.v_pool.abs().max().float() / TOP[kind]).reshape(1)
+        else:
+            km = torch.empty((NB, BS, H), dtype=torch.float32, device="cuda")
+            vm = torch.empty_like(km)
         slots = torch.arange(NB * BS, dtype=torch.int64, device="cuda")
         P.kv_append(wl.k_pool.reshape(NB * BS, H, D), wl.v_pool.reshape(NB * BS, H, D), slots,
-                    kc, vc, km, vm, cache_dtype=kind)
+                    kc, vc, km, vm, cache_dtype=kind, scale_strides=strides)
         torch.cuda.synchronize()
         wl.k_pool = wl.v_pool = None               # the bf16 pools are no longer needed
         pools.append((wl, kc, vc, km, vm))
@@ -471,7 +481,7 @@ def run_fp8_decode(args, P, W, kind="fp8"):
         d = dev[i % N_LAYERS]
         P.paged_decode(w.q, kc, vc, d["bt"], d["ctx"], int(w.ctx_before.max()), w.sm_scale,
                        k_meta=km, v_meta=vm, partition_size=args.partition_size, workspace=ws,
-                       out=d["out"], cache_dtype=kind)
+                       out=d["out"], cache_dtype=kind, scale_strides=strides)
 
     for i in range(args.warmup):
         call(i)
@@ -487,15 +497,16 @@ def run_fp8_decode(args, P, W, kind="fp8"):
     algs = []
     for w, *_ in pools:
         w.ctx_after = w.ctx_before                 # decode only: the pools hold ctx_before tokens
-        algs.append(decode_bytes(w, 2 * (D + 4))[0])   # D codes + one fp32 scale, K and V
+        # D codes + one fp32 scale per row, K and V (a per-tensor scale is one value per call)
+        algs.append(decode_bytes(w, 2 * D if per_tensor else 2 * (D + 4))[0])
     alg = float(sum(algs) / len(algs))
     st = stats_us(ms)
     tokens = int(sum(int(w.ctx_before.sum()) for w, *_ in pools) / N_LAYERS)
     config = {"workload": name, "batch": B, "num_q_heads": Hq, "num_kv_heads": H,
               "head_dim": D, "block_size": wl0.block_size, "context": "U{512..4096}",
-              "cache": f"{label} + fp32 per-row scale", "query": "bf16",
+              "cache": f"{label} + fp32 {'per-tensor' if per_tensor else 'per-row'} scale", "query": "bf16",
               "layers_rotated": N_LAYERS, "partition_size": args.partition_size or "auto"}
-    rec = base_record(args, f"paged decode KV GB/s ({label} cache)",
+    rec = base_record(args, f"paged decode KV GB/s ({label} cache{', per-tensor scale' if per_tensor else ''})",
                       alg / (st["mean"] * 1e-6) / 1e9, "GB/s", ms_per_step, "bf16", config)
     rec.update({"decode_us": st, "context_tokens_per_s": round(tokens / (st["mean"] * 1e-6), 1),
                 "roofline": hbm_roofline(f"paged_decode (decode_kernel {kind} + merge_kernel)", alg,
@@ -620,7 +631,8 @@ WORKLOADS = {"llama8b-decode-step": run_llama8b, "mixed-append-fp8": run_mixed_a
              "pack3-exhaustive": run_pack3_exhaustive, "copy-calibration": run_copy_calibration,
              "fp8-decode": run_fp8_decode, "dual-stacked-decode": run_dual_stacked,
              "e5m2-decode": lambda a, P, W: run_fp8_decode(a, P, W, "e5m2"),
-             "int8-decode": lambda a, P, W: run_fp8_decode(a, P, W, "i8")}
+             "int8-decode": lambda a, P, W: run_fp8_decode(a, P, W, "i8"),
+             "fp8-tensor-scale-decode": lambda a, P, W: run_fp8_decode(a, P, W, "fp8", True)}
 
 
 def main():
