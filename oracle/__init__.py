@@ -27,7 +27,7 @@ from .quant3 import quantize_u3_rows, dequantize_u3_rows
 from .quant8 import (e5m2_decode_table, e5m2_decode, e5m2_encode_rne, quantize_e5m2_rows,
                      quantize_int8_rows, dequantize_e5m2_rows, dequantize_int8_rows, E5M2_MAX,
                      INT8_MAX, quantize_given_scale, scale_offsets)
-from .slots import decode_slot_mapping, prefill_slot_mapping
+from .slots import decode_slot_mapping, prefill_slot_mapping, slot_mapping_ref
 from .append import append_ref, CacheSpec
 from .attention import (paged_decode_ref, paged_decode_split_ref, lse_merge_ref,
                         gather_rows_f64, PoolView)
@@ -39,6 +39,6 @@ __all__ = [
     "e5m2_decode_table", "e5m2_decode", "e5m2_encode_rne", "quantize_e5m2_rows",
     "quantize_int8_rows", "dequantize_e5m2_rows", "dequantize_int8_rows", "E5M2_MAX", "INT8_MAX",
     "quantize_given_scale", "scale_offsets",
-    "decode_slot_mapping", "prefill_slot_mapping", "append_ref", "CacheSpec",
+    "decode_slot_mapping", "prefill_slot_mapping", "slot_mapping_ref", "append_ref", "CacheSpec",
     "paged_decode_ref", "paged_decode_split_ref", "lse_merge_ref", "gather_rows_f64", "PoolView",
 ]

@@ -47,3 +47,33 @@ def prefill_slot_mapping(block_tables: np.ndarray, starts, counts, block_size: i
     if pad_mask is not None:
         out[np.asarray(pad_mask, dtype=bool)] = -1
     return out
+
+
+def slot_mapping_ref(token_request, token_position, block_tables, block_size: int,
+                     batch: int) -> np.ndarray:
+    """Slot id of every new token, from its request and position (the launcher's step).
+
+    [Append] Inputs items 6 and 7 and step 9: with a block table, token t of request r at
+    position p goes to block_tables[r, p // block_size] * block_size + p % block_size.
+    Without one (block_tables None), the contiguous cache [batch, num_kv_heads, max_seq_len,
+    head_dim] is meant and the id is r * max_seq_len + p with block_size = max_seq_len (the
+    encoding of [Append] step 5; a reading, as Inputs item 6 states another).
+    Readings: a token whose request is negative (padding), at or beyond `batch`, or whose
+    position is negative or outside its table row (or >= max_seq_len) gets -1, so the append
+    skips it.  token_request None means token t belongs to request t (one decode token each).
+    """
+    pos = np.asarray(token_position, dtype=np.int64)
+    req = np.arange(pos.shape[0]) if token_request is None else np.asarray(token_request, np.int64)
+    out = np.full(pos.shape[0], -1, dtype=np.int64)
+    for t in range(pos.shape[0]):
+        r, p = int(req[t]), int(pos[t])
+        if r < 0 or r >= batch or p < 0:
+            continue
+        if block_tables is None:
+            if p < block_size:
+                out[t] = r * block_size + p
+            continue
+        row = np.asarray(block_tables)[r]
+        if p // block_size < row.shape[0]:
+            out[t] = _slot(row, block_size, p)
+    return out

@@ -142,3 +142,73 @@ def test_workload_shapes():
     assert 4000 < m.slot_mapping.numel() < 17000 and m.block_size == 32
     lc = W.long_context("cpu", batch=2, ctx_lo=64, ctx_hi=200)
     assert lc.group == 8 and lc.block_size == 64
+
+
+# ---- per-token slot ids from (request, position): the launcher's step, built on the device
+# by build_slot_mapping ("Write Triton Kv Cache Append Kernel", Inputs items 6-7, step 9)
+
+from oracle import slot_mapping_ref
+
+
+def test_slot_mapping_ref_agrees_with_allocator_and_page_forms():
+    wl = W.mixed_append("cpu")
+    got = slot_mapping_ref(wl.token_request.numpy(), wl.token_position.numpy(), wl.block_tables.numpy(),
+                           wl.block_size, len(wl.req_start))
+    assert np.array_equal(got, wl.slot_mapping.numpy())
+    d = W.llama8b_decode("cpu", make_pool=False)
+    got = slot_mapping_ref(None, d.ctx_before.numpy(), d.block_tables.numpy(), d.block_size, d.batch)
+    assert np.array_equal(got, d.slot_mapping.numpy())
+    assert np.array_equal(got, decode_slot_mapping(d.block_tables.numpy(), d.ctx_before.numpy(),
+                                                   d.block_size))
+
+
+def test_slot_mapping_ref_worked_by_hand():
+    bt = np.array([[7, 2, 0], [4, 9, 0]], np.int32)          # block size 16, 3 table entries
+    req = np.array([0, 0, 1, 1, -1, 2, 0, 1], np.int64)
+    pos = np.array([0, 17, 15, 31, 5, 0, 48, -1], np.int64)
+    # 0 -> 7*16+0; 17 -> block 2, +1; 15 -> 4*16+15; 31 -> 9*16+15; padding; request 2 of 2;
+    # position 48 = table entry 3 (outside the row); negative position
+    assert slot_mapping_ref(req, pos, bt, 16, 2).tolist() == [112, 33, 79, 159, -1, -1, -1, -1]
+    # contiguous cache, max_seq_len 64: r * 64 + p, positions >= 64 rejected
+    pos2 = np.array([0, 17, 15, 63, 5, 0, 64, 3], np.int64)
+    assert slot_mapping_ref(req, pos2, None, 64, 3).tolist() == [0, 17, 79, 127, -1, 128, -1, 67]
+
+
+def test_contiguous_cache_through_the_paged_oracle():
+    """The contiguous cache [B, Hkv, S, D] with slot r*S + p is the paged pool of block size S
+    whose block r is request r, seen through the (request, position, head) transposed view:
+    the oracle's append writes cache[r, h, p] = new[t, h], and its decode over that view equals
+    its decode over a shuffled paged copy of the same rows."""
+    B, H, S, D, BS = 3, 2, 64, 8, 16
+    rng = np.random.default_rng(11)
+    cache_k = np.zeros((B, H, S, D), np.uint16)
+    cache_v = np.zeros((B, H, S, D), np.uint16)
+    lens = [5, 64, 33]
+    req = np.concatenate([np.full(n, r) for r, n in enumerate(lens)])
+    pos = np.concatenate([np.arange(n) for n in lens])
+    slots = slot_mapping_ref(req, pos, None, S, B)
+    new_k = rng.integers(0x3C00, 0x4400, (len(req), H, D)).astype(np.uint16)   # fp16 in [1, 4)
+    new_v = rng.integers(0xBC00, 0xC400, (len(req), H, D)).astype(np.uint16)
+    view_k, view_v = cache_k.transpose(0, 2, 1, 3), cache_v.transpose(0, 2, 1, 3)
+    append_ref(new_k, new_v, slots, view_k, view_v, CacheSpec("same", "f16"), S)
+    for t in range(len(req)):
+        assert np.array_equal(cache_k[req[t], :, pos[t]], new_k[t])
+        assert np.array_equal(cache_v[req[t], :, pos[t]], new_v[t])
+    q = rng.standard_normal((B, 4, D))
+    want = paged_decode_ref(q, PoolView("same", view_k, dtype="f16"), PoolView("same", view_v, dtype="f16"),
+                            np.arange(B).reshape(B, 1), np.array(lens), S, H, 0.3)
+    # the same rows in a shuffled paged pool of 16-token blocks
+    nblk = B * S // BS
+    perm = rng.permutation(nblk)
+    pk = np.zeros((nblk, BS, H, D), np.uint16)
+    pv = pk.copy()
+    bt = np.zeros((B, S // BS), np.int32)
+    for r in range(B):
+        for j in range(S // BS):
+            blk = perm[r * (S // BS) + j]
+            bt[r, j] = blk
+            pk[blk] = view_k[r, j * BS:(j + 1) * BS]
+            pv[blk] = view_v[r, j * BS:(j + 1) * BS]
+    got = paged_decode_ref(q, PoolView("same", pk, dtype="f16"), PoolView("same", pv, dtype="f16"), bt,
+                           np.array(lens), BS, H, 0.3)
+    assert np.allclose(got, want, rtol=0, atol=1e-12)
