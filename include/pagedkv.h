@@ -86,7 +86,11 @@ typedef enum {
  *                    v_cache = base + num_kv_heads*block_size*head_dim, c_stride_block =
  *                    2*num_kv_heads*block_size*head_dim, c_stride_slot = head_dim,
  *                    c_stride_head = block_size*head_dim); k_cache and v_cache share the
- *                    strides.
+ *                    strides.  The contiguous cache [batch, num_kv_heads, max_seq_len,
+ *                    head_dim] with slot = request*max_seq_len + position ([Append] step 5)
+ *                    is the pool whose block is one request: num_blocks = batch, block_size =
+ *                    max_seq_len (a power of two), c_stride_block = num_kv_heads*max_seq_len*
+ *                    head_dim, c_stride_slot = head_dim, c_stride_head = max_seq_len*head_dim.
  *   cache_dtype      == in_dtype (bit copy), or PKV_FP8_E4M3FN, PKV_FP8_E5M2, PKV_INT8
  *                    (the byte-code caches: pools 8-byte aligned, strides multiples of 8),
  *                    or PKV_U3.
@@ -99,7 +103,8 @@ typedef enum {
  *                    (s = fp16((max-min)/7), z = fp16(-min/s), q = clamp(rint(x/s+z),
  *                    0, 7); degenerate rows use s = 1, z = fp16(-min)).  Contiguous.
  *                    NULL for same-dtype caches.
- *   head_dim         64 or 128.   block_size 16, 32 or 64.   num_tokens >= 0, and
+ *   head_dim         64 or 128.   block_size a power of two from 16 to 2^24 (paged_decode
+ *                    reads pools of 16, 32 or 64).   num_tokens >= 0, and
  *                    num_tokens * num_kv_heads < 2^31 (else PKV_EUNSUPPORTED).
  * Inputs must be finite for the quantised caches.  Bit-exact by contract.
  */
@@ -236,6 +241,30 @@ int paged_decode_scaled(void* out, const void* q, pkv_dtype q_dtype,
                         int batch, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                         int64_t num_blocks, int max_context_len, float sm_scale, int partition_size,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * build_slot_mapping - the slot id of every new token from its request and position.
+ *
+ * Defined by [Append], Inputs items 6 and 7 and Required reasoning process step 9 (the
+ * launcher's step: paged slot = block_id * block_size + slot_in_block with the physical block
+ * of the token's logical block; a decode token's position is the context length before the
+ * increment).
+ *   token_request    device int32 [num_tokens], or NULL: token t belongs to request t (one
+ *                    decode token per request).  A negative entry marks a padding token.
+ *   token_position   device int32 [num_tokens], the token's position in its sequence.
+ *   block_tables     device int32 [batch, bt_stride_b] (bt_stride_b >= 1): slot =
+ *                    block_tables[r, p / block_size] * block_size + p % block_size.  NULL: the
+ *                    contiguous cache, slot = r * block_size + p with block_size = max_seq_len.
+ *   block_size       a power of two from 16 to 2^24.
+ *   slot_mapping     device int64 [num_tokens], written.  -1 where the request is negative or
+ *                    >= batch, or the position is negative, outside the table row (p /
+ *                    block_size >= bt_stride_b) or, without a table, >= block_size: kv_append
+ *                    then skips the token.
+ * num_tokens < 2^31.  Bit-exact.  Entries of the table row beyond the position's block are not read.
+ */
+int build_slot_mapping(const int32_t* token_request, const int32_t* token_position, int64_t num_tokens,
+                       const int32_t* block_tables, int64_t bt_stride_b, int batch, int block_size,
+                       int64_t* slot_mapping, hipStream_t stream);
 
 /*
  * pack3 / unpack3 - 3-bit packing, [3bit] sections 1A and 1B: value j of each group

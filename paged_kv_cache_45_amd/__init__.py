@@ -8,7 +8,7 @@ an exception is raised.
 
 Entry points (same names as the C ABI):
     kv_append, kv_append_scaled, paged_decode, paged_decode_scaled,
-    paged_decode_workspace_size, pack3, unpack3, pkv_status_string
+    paged_decode_workspace_size, build_slot_mapping, pack3, unpack3, pkv_status_string
 """
 from __future__ import annotations
 
@@ -17,7 +17,7 @@ import math
 import os
 from typing import Optional
 
-__all__ = ["kv_append", "kv_append_scaled", "paged_decode", "paged_decode_scaled", "paged_decode_workspace_size", "pack3", "unpack3",
+__all__ = ["kv_append", "kv_append_scaled", "paged_decode", "paged_decode_scaled", "build_slot_mapping", "paged_decode_workspace_size", "pack3", "unpack3",
            "pkv_status_string", "decode_workspace", "library_path", "load_library",
            "PKV_F16", "PKV_BF16", "PKV_FP8_E4M3FN", "PKV_U3", "PKV_FP8_E5M2", "PKV_INT8",
            "PagedKVError"]
@@ -68,6 +68,8 @@ def load_library() -> ctypes.CDLL:
     lib.paged_decode_scaled.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, vp, i32, i64, i64, i64,
                                         vp, vp, i64, i64, i64, vp, i64, vp, i32, i32, i32, i32, i32,
                                         i64, i32, f32, i32, vp, sz, vp]
+    lib.build_slot_mapping.restype = i32
+    lib.build_slot_mapping.argtypes = [vp, vp, i64, vp, i64, i32, i32, vp, vp]
     lib.pack3.restype = i32
     lib.pack3.argtypes = [vp, vp, i64, vp]
     lib.unpack3.restype = i32
@@ -238,6 +240,23 @@ def paged_decode_scaled(q, k_cache, v_cache, k_scale, v_scale, scale_strides, bl
     """paged_decode over a byte-code cache with caller-given scales (see kv_append_scaled)."""
     return paged_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len,
                         k_meta=k_scale, v_meta=v_scale, scale_strides=scale_strides, **kw)
+
+
+def build_slot_mapping(token_position, block_size: int, batch: int, block_tables=None,
+                       token_request=None, out=None, stream=None):
+    """int64 slot ids [T] of new tokens from int32 positions [T] (and int32 requests [T], or
+    None for request t = token t): paged through block_tables [batch, max_blocks], or the
+    contiguous cache's request * block_size + position without a table; -1 for padding."""
+    import torch
+    T = token_position.numel()
+    if out is None:
+        out = torch.empty(T, dtype=torch.int64, device=token_position.device)
+    bts = 0 if block_tables is None else block_tables.stride(0)
+    st = load_library().build_slot_mapping(_ptr(token_request), _ptr(token_position), T,
+                                           _ptr(block_tables), bts, int(batch), int(block_size),
+                                           _ptr(out), _stream(stream))
+    _check("build_slot_mapping", st)
+    return out
 
 
 def pack3(values, packed=None, stream=None):

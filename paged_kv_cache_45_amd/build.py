@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libpagedkv.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.cpp", "pack3.hip", "append.hip", "decode.hip",
+SOURCES = ["api.cpp", "pack3.hip", "append.hip", "slots.hip", "decode.hip",
            "decode_same_d128.hip", "decode_u3_d128.hip", "decode_fp8_d128.hip",
            "decode_same_d64.hip", "decode_u3_d64.hip", "decode_fp8_d64.hip",
            "decode_e5m2_d128.hip", "decode_i8_d128.hip", "decode_e5m2_d64.hip", "decode_i8_d64.hip"]

@@ -30,6 +30,13 @@ int check_block_size(int bs) {
   if (bs <= 0 || log2_exact(bs) < 0) return PKV_EINVAL;
   return (bs == 16 || bs == 32 || bs == 64) ? PKV_OK : PKV_EUNSUPPORTED;
 }
+// The append and the slot builder take any power-of-two block from 16 to 2^24 tokens: the
+// contiguous cache is the pool whose block is one request's whole sequence.
+constexpr int kMaxAppendBlock = 1 << 24;
+int check_append_block_size(int bs) {
+  if (bs <= 0 || log2_exact(bs) < 0) return PKV_EINVAL;
+  return (bs >= 16 && bs <= kMaxAppendBlock) ? PKV_OK : PKV_EUNSUPPORTED;
+}
 bool is16(pkv_dtype t) { return t == PKV_F16 || t == PKV_BF16; }
 bool known(pkv_dtype t) {
   return t == PKV_F16 || t == PKV_BF16 || t == PKV_FP8_E4M3FN || t == PKV_U3 || t == PKV_FP8_E5M2 ||
@@ -119,6 +126,30 @@ const char* pkv_status_string(int status) {
   }
 }
 
+int build_slot_mapping(const int32_t* token_request, const int32_t* token_position, int64_t num_tokens,
+                       const int32_t* block_tables, int64_t bt_stride_b, int batch, int block_size,
+                       int64_t* slot_mapping, hipStream_t stream) {
+  if (num_tokens < 0 || batch < 0) return PKV_EINVAL;
+  if (num_tokens >= (int64_t(1) << 31)) return PKV_EUNSUPPORTED;
+  const int st = check_append_block_size(block_size);
+  if (st != PKV_OK) return st;
+  if (num_tokens == 0) return PKV_OK;
+  if (!token_position || !slot_mapping || !aligned(token_position, 4) || !aligned(slot_mapping, 8))
+    return PKV_EINVAL;
+  if (token_request && !aligned(token_request, 4)) return PKV_EINVAL;
+  if (block_tables && (!aligned(block_tables, 4) || bt_stride_b <= 0)) return PKV_EINVAL;
+  pkv::SlotParams p{};
+  p.token_request = token_request;
+  p.token_position = token_position;
+  p.num_tokens = num_tokens;
+  p.block_tables = block_tables;
+  p.bt_sb = bt_stride_b;
+  p.batch = batch;
+  p.log2_bs = log2_exact(block_size);
+  p.slot_mapping = slot_mapping;
+  return pkv::launch_slots(p, stream) == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
 int pack3(const uint8_t* values, uint8_t* packed, int64_t n_values, hipStream_t stream) {
   if (n_values < 0 || n_values % 8) return PKV_EINVAL;
   if (n_values == 0) return PKV_OK;
@@ -155,7 +186,7 @@ static int append_impl(const void* k_new, const void* v_new, pkv_dtype in_dtype,
   if (num_tokens >= (int64_t(1) << 31) / num_kv_heads) return PKV_EUNSUPPORTED;
   int st = check_head_dim(head_dim);
   if (st != PKV_OK) return st;
-  st = check_block_size(block_size);
+  st = check_append_block_size(block_size);
   if (st != PKV_OK) return st;
   if (num_tokens == 0) return PKV_OK;   // nothing to read or write (source pointers may be NULL)
   if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PKV_EINVAL;

@@ -66,6 +66,17 @@ struct DecodeParams {
   int log2_claim;                     // ... in units of 2^log2_claim tokens inside one block
 };
 
+struct SlotParams {
+  const int32_t* token_request;       // nullptr: token t belongs to request t
+  const int32_t* token_position;
+  int64_t num_tokens;
+  const int32_t* block_tables;        // nullptr: contiguous cache, slot = request * 2^log2_bs + position
+  int64_t bt_sb;
+  int batch;
+  int log2_bs;
+  int64_t* slot_mapping;
+};
+
 // Launch geometry of paged_decode.
 struct DecodePlan {
   int hpi;                            // kv heads per wave instruction
@@ -79,6 +90,7 @@ struct DecodePlan {
   size_t lds_bytes;                   // dynamic LDS of the decode kernel
 };
 
+hipError_t launch_slots(const SlotParams& p, hipStream_t s);
 hipError_t launch_pack3(const uint8_t* values, uint8_t* packed, int64_t n_values, hipStream_t s);
 hipError_t launch_unpack3(const uint8_t* packed, uint8_t* values, int64_t n_values, hipStream_t s);
 

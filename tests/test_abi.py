@@ -57,7 +57,7 @@ def _append(lib, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(k_new=None), -1), (dict(slots=None), -1), (dict(T=-1), -1), (dict(T=0, k_new=None, slots=None), 0), (dict(in_dtype=2), -2),
     (dict(in_dtype=0, cdt=1), -1), (dict(D=96), -2), (dict(D=0), -1), (dict(bs=12), -1),
-    (dict(bs=128), -2), (dict(ks_h=4), -1), (dict(k_new=FAKE8), -1), (dict(cdt=2), -1),
+    (dict(bs=1 << 25), -2), (dict(bs=8), -2), (dict(ks_h=4), -1), (dict(k_new=FAKE8), -1), (dict(cdt=2), -1),
     (dict(cdt=3), -1), (dict(nb=0), -1), (dict(H=0), -1), (dict(in_dtype=9), -1),
     (dict(T=(1 << 31) // 8), -2),
     (dict(ch=-128), -1),
@@ -164,3 +164,18 @@ def _decode_scaled(lib, **kw):
 ])
 def test_decode_scaled_validation(lib, kw, status):
     assert _decode_scaled(lib, **kw) == status
+
+
+def _slots(lib, **kw):
+    a = dict(req=FAKE, pos=FAKE, T=16, bt=FAKE, bts=8, B=4, bs=16, out=FAKE, stream=None)
+    a.update(kw)
+    return lib.build_slot_mapping(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(pos=None), -1), (dict(out=None), -1), (dict(T=-1), -1), (dict(T=0, pos=None), 0),
+    (dict(bs=12), -1), (dict(bs=8), -2), (dict(bs=1 << 25), -2), (dict(bts=0), -1),
+    (dict(T=1 << 31), -2), (dict(B=-1), -1), (dict(out=FAKE + 4), -1), (dict(pos=FAKE + 2), -1),
+])
+def test_build_slot_mapping_validation(lib, kw, status):
+    assert _slots(lib, **kw) == status
