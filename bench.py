@@ -26,6 +26,7 @@ of the remaining shapes:
   e5m2-decode        the same over fp8 e5m2 pools
   int8-decode        the same over int8 pools
   fp8-tensor-scale-decode  the fp8 e4m3fn pools with one caller-given scale per pool
+  contiguous-decode  the Llama-8B decode shape over a contiguous [B, Hkv, 4096, D] cache
                      (KV GB/s; the pools hold half the bytes of the bf16 ones)
   dual-stacked-decode  the Llama-8B decode shape over the dual-stacked block layout
                      [num_blocks, 2, num_kv_heads, block_size, head_dim], as strided views (KV GB/s)
@@ -514,6 +515,74 @@ def run_fp8_decode(args, P, W, kind="fp8", per_tensor=False):
     return rec
 
 
+def run_contiguous(args, P, W):
+    """paged_decode at the Llama-8B shape over the contiguous cache [batch, num_kv_heads,
+    max_seq_len = 4352, head_dim] (room for the longest context, 4097 tokens, in whole 16-token
+    blocks), read through a virtual block table (virtual block b * Hkv * S / 16 + j = tokens
+    16 j .. 16 j + 15 of request b, block stride 16 D, head stride S D); four layer caches in
+    rotation."""
+    import torch
+    S, VBS = 4352, 16
+    layers = []
+    for i in range(N_LAYERS):
+        wl = W.llama8b_decode("cuda", data_seed=W.BASE_SEED + 2 + 1000 * i, poison=False)
+        NB, BS, H, D = wl.k_pool.shape
+        B = wl.batch
+        caches = []
+        for pool in (wl.k_pool, wl.v_pool):
+            c = torch.zeros((B, H, S, D), dtype=wl.dtype, device="cuda")
+            for b, blks in enumerate(wl.blocks_of):
+                assert len(blks) * BS <= S, "context longer than the contiguous cache"
+                rows = pool[torch.tensor(blks, device="cuda")].reshape(len(blks) * BS, H, D)
+                c[b, :, :rows.shape[0]] = rows.permute(1, 0, 2)
+            caches.append(c)
+        torch.cuda.synchronize()
+        wl.k_pool = wl.v_pool = None
+        nbv = (B - 1) * H * S // VBS + S // VBS
+        views = [torch.as_strided(c, (nbv, VBS, H, D), (VBS * D, D, S * D, 1)) for c in caches]
+        table = (torch.arange(B, dtype=torch.int32)[:, None] * (H * S // VBS)
+                 + torch.arange(S // VBS, dtype=torch.int32)[None, :]).cuda()
+        layers.append((wl, caches, views, table, wl.ctx_before.cuda(), torch.empty_like(wl.q)))
+    wl0 = layers[0][0]
+    B, Hq, H, D = wl0.batch, wl0.num_q_heads, wl0.num_kv_heads, wl0.head_dim
+    maxctx = max(int(l[0].ctx_before.max()) for l in layers)
+    ws = P.decode_workspace(B, Hq, H, D, maxctx, args.partition_size)
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        w, _, views, table, ctx, out = layers[i % N_LAYERS]
+        P.paged_decode(w.q, views[0], views[1], table, ctx, int(w.ctx_before.max()), w.sm_scale,
+                       partition_size=args.partition_size, workspace=ws, out=out)
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(i)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = event_times_ms(call, args.steps, stream)
+    for l in layers:
+        assert torch.isfinite(l[5].float()).all(), "non-finite decode output"
+    algs = []
+    for l in layers:
+        w = l[0]
+        w.ctx_after = w.ctx_before
+        algs.append(decode_bytes(w, 2 * D * 2)[0])
+    alg = float(sum(algs) / len(algs))
+    st = stats_us(ms)
+    config = {"workload": "contiguous-decode", "batch": B, "num_q_heads": Hq, "num_kv_heads": H,
+              "head_dim": D, "max_seq_len": S, "context": "U{512..4096}",
+              "layout": "[batch, num_kv_heads, max_seq_len, head_dim], virtual 16-token blocks",
+              "layers_rotated": N_LAYERS, "partition_size": args.partition_size or "auto"}
+    rec = base_record(args, "paged decode KV GB/s (contiguous cache)",
+                      alg / (st["mean"] * 1e-6) / 1e9, "GB/s", ms_per_step, "bf16", config)
+    rec.update({"decode_us": st, "roofline": hbm_roofline("paged_decode (decode_kernel + merge_kernel)", alg,
+                                                          ms.mean() * 1e-3)})
+    return rec
+
+
 def run_dual_stacked(args, P, W):
     """paged_decode at the Llama-8B shape over the dual-stacked block layout
     [num_blocks, 2, num_kv_heads, block_size, head_dim] (K and V of a block in one buffer,
@@ -632,7 +701,8 @@ WORKLOADS = {"llama8b-decode-step": run_llama8b, "mixed-append-fp8": run_mixed_a
              "fp8-decode": run_fp8_decode, "dual-stacked-decode": run_dual_stacked,
              "e5m2-decode": lambda a, P, W: run_fp8_decode(a, P, W, "e5m2"),
              "int8-decode": lambda a, P, W: run_fp8_decode(a, P, W, "i8"),
-             "fp8-tensor-scale-decode": lambda a, P, W: run_fp8_decode(a, P, W, "fp8", True)}
+             "fp8-tensor-scale-decode": lambda a, P, W: run_fp8_decode(a, P, W, "fp8", True),
+             "contiguous-decode": run_contiguous}
 
 
 def main():
