@@ -14,7 +14,7 @@ Pages cited:
   [3bit] "triton-3bit-kv-cache-kernel" README, title paragraph (the fused 3-bit
     flash-decoding reads codes and dequantises them on the fly).
 
-Readings (listed in DESIGN.md): q head h reads kv head h // (Hq / Hkv); a request
+Readings (where the pages leave a step open): q head h reads kv head h // (Hq / Hkv); a request
 with context length 0 produces an all-zero output; block-table entries at or
 beyond cdiv(L, block_size) are never read; split-K partitions are the token
 ranges [P*i, P*(i+1)) counted from token 0, merged by log-sum-exp.

@@ -13,7 +13,7 @@ with mantissa 7 reserved for NaN, largest finite magnitude 1.75 * 2^8 = 448, and
 subnormals m * 2^-9 for exponent field 0.  The format table and the encoder
 below are written from that definition.
 
-Readings of the pages (all listed in the design doc):
+Readings of the pages (taken where they leave a step open):
   * per-token-per-head scale s = absmax / 448 computed by the append itself over
     its own head_dim vector; s = 1 when the vector is all zero;
   * y = x / s in fp32 (correctly rounded), clamped to [-448, 448], then rounded to

@@ -6,7 +6,7 @@ test 3 (fp16 affine dequant x_hat = (q - z) * s and the requant identity
 clamp(round(x_hat / s + z), 0, 7) == q).
 
 The page fixes only the dequantisation identity and fp16 scale/zero.  The rule
-for choosing s and z is our reading (listed in the design doc): asymmetric min-max
+for choosing s and z is our reading (the README leaves it open): asymmetric min-max
 per (token, kv head) vector with a floating zero point in code units.  All steps
 in float32, in this order, with no fused multiply-add:
 

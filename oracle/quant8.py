@@ -12,7 +12,7 @@ bits; exponent field 31 holds the infinities (mantissa 0) and NaNs; the largest 
 magnitude is 1.75 * 2^15 = 57344; exponent field 0 holds the subnormals m * 2^-16.  The
 table below is written from that definition and the encoder searches it.
 
-Readings of the pages (listed in the design doc), by analogy with the e4m3fn cache:
+Readings of the pages (taken where they leave a step open), by analogy with the e4m3fn cache:
   * one fp32 scale per (block, slot, kv head), computed by the append from its own row:
     s = absmax / 57344 (e5m2) or s = absmax / 127 (int8); s = 1 for an all-zero row;
   * y = x / s in fp32 (correctly rounded);
