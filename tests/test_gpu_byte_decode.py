@@ -231,3 +231,55 @@ def test_given_per_tensor_fp8_llama8b_full_size_sampled():
                             wl.block_size, wl.num_kv_heads, wl.sm_scale, heads=heads)
     sel = np.array([b for b, _ in heads]), np.array([h for _, h in heads])
     assert report("fp8 per-tensor llama8b", f32_of(out)[sel], want[sel], wl.dtype) <= ATTN_TOL
+
+
+@pytest.mark.parametrize("kind", ["fp8", "e5m2", "i8"])
+@pytest.mark.parametrize("G,D,bs,dtype", [(8, 64, 64, torch.float16), (1, 128, 32, torch.float16),
+                                          (2, 64, 16, torch.bfloat16)])
+def test_given_scales_shapes(kind, G, D, bs, dtype):
+    """Per-block-and-head scales at other group sizes, head dims, block sizes and query types;
+    ragged and empty contexts; two partition sizes."""
+    P = need_gpu()
+    lens = [0, 1, 63, 64, 65, 700, 129]
+    wl = W.decode_workload(f"{kind}-given", batch=len(lens), num_q_heads=4 * G, num_kv_heads=4,
+                           head_dim=D, block_size=bs, ctx_lo=0, ctx_hi=0, dtype=dtype, device="cuda",
+                           seed=600 + G + D + bs, append_one=False, ctx_override=lens, poison=False)
+    gpu, strides, kpool, vpool = _given_scale_case(P, wl, kind, "block_head", seed=G + D)
+    want = paged_decode_ref(f32_of(wl.q), kpool, vpool, wl.block_tables.numpy(), np.array(lens),
+                            wl.block_size, wl.num_kv_heads, wl.sm_scale)
+    for ps in (0, 64):
+        out = P.paged_decode_scaled(wl.q, gpu[0], gpu[1], gpu[2], gpu[3], strides,
+                                    wl.block_tables.cuda(), wl.ctx_after.cuda(), max(lens),
+                                    sm_scale=wl.sm_scale, partition_size=ps, cache_dtype=kind)
+        got = f32_of(out)
+        assert np.all(got[0] == 0)
+        assert report(f"{kind} given G{G} D{D} bs{bs} {dtype} ps{ps}", got, want, dtype) <= ATTN_TOL
+
+
+def test_append_scaled_padding_and_out_of_range_slots():
+    """kv_append_scaled skips slot -1 and slots past the pool, touches nothing else, and leaves
+    the scale arrays unchanged; an empty call is a no-op."""
+    P = need_gpu()
+    from gpu_helpers import bits16 as _b16
+    NB, BS, H, D = 6, 16, 2, 128
+    g = torch.Generator().manual_seed(W.BASE_SEED + 64)
+    T = 40
+    new_k = torch.randn((T, H, D), generator=g).to(torch.bfloat16)
+    new_v = torch.randn((T, H, D), generator=g).to(torch.bfloat16)
+    slots = torch.randperm(NB * BS, generator=g)[:T].to(torch.int64)
+    slots[::5] = -1
+    slots[3] = NB * BS + 7                                   # past the pool: skipped
+    ks = torch.rand(NB * H, generator=g) * 0.02 + 0.005
+    vs = torch.rand(NB * H, generator=g) * 0.02 + 0.005
+    kc = torch.randint(0, 256, (NB, BS, H, D), generator=g, dtype=torch.int32).to(torch.uint8)
+    vc = torch.randint(0, 256, (NB, BS, H, D), generator=g, dtype=torch.int32).to(torch.uint8)
+    hk, hv = kc.numpy().copy(), vc.numpy().copy()
+    dk, dv, dks, dvs = kc.cuda(), vc.cuda(), ks.cuda(), vs.cuda()
+    P.kv_append_scaled(new_k[:0].cuda(), new_v[:0].cuda(), slots[:0].cuda(), dk, dv, dks, dvs, (H, 0, 1),
+                       cache_dtype="i8")
+    P.kv_append_scaled(new_k.cuda(), new_v.cuda(), slots.cuda(), dk, dv, dks, dvs, (H, 0, 1), cache_dtype="i8")
+    torch.cuda.synchronize()
+    append_ref(_b16(new_k), _b16(new_v), slots.numpy(), hk, hv, CacheSpec("i8", "bf16"), BS,
+               ks.numpy().copy(), vs.numpy().copy(), scale_strides=(H, 0, 1))
+    assert np.array_equal(dk.cpu().numpy(), hk) and np.array_equal(dv.cpu().numpy(), hv)
+    assert torch.equal(dks.cpu(), ks) and torch.equal(dvs.cpu(), vs)
