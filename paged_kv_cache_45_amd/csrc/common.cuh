@@ -83,7 +83,11 @@ enum : int {
   DPP_QUAD_NEXT = 0xF9,      // quad_perm [1,2,3,3]: lane j reads lane j+1 of its quad
   DPP_ROW_HALF_MIRROR = 0x141,
   DPP_ROW_MIRROR = 0x140,
+  DPP_ROW_ROR4 = 0x124,      // lane i of a 16-lane row reads lane (i + 4) mod 16
+  DPP_ROW_ROR8 = 0x128,      // lane i of a 16-lane row reads lane (i + 8) mod 16
 };
+// quad_perm [g, g, g, g]: every lane of a quad reads lane g of the quad
+template <int g> constexpr int dpp_quad_bcast() { return g | (g << 2) | (g << 4) | (g << 6); }
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {

@@ -115,6 +115,9 @@ struct State {
   uint32_t qv[G][4];                 // this lane's 8 query elements of each query head
   float qsum[G];                     // u3: sum of the query row (dequant hoisting)
   float m[G], l[G], zc[G];
+  // own-head form (see own_head_form): this lane's query head's running max, sum, zero-point
+  // term and query sum; m, l and zc above hold every head's values again from range end on
+  float mo, lo, zco, qso;
   // accumulator column e (this lane's d = 8c + e) of query head g is acc4[g / 4][e][g % 4]: the
   // register quads are the C operands of the PV matrix-core products
   f32x4_t acc4[(G + 3) / 4][8];
@@ -131,6 +134,45 @@ struct State {
 // With G = 8 the extra operand registers push the kernel into spills (measured 7 % slower on
 // the long-context decode), so G = 8 keeps the FMA form.
 constexpr int kMfmaMaxG = 4;
+
+// Own-head form (2 or 4 query heads per kv head, 16 lanes per row): after the score products a
+// reduce-scatter over the quad (two DPP stages that halve the head set) and a sum over the four
+// quads of the row (two rotations) leave in lane q of every quad the full score of query head
+// q mod G, instead of every head's score in every lane.  The online softmax then runs for one
+// head per lane (a quarter of the exponentials for G = 4), the matrix-core PV takes its A
+// operand straight from that lane, and the per-head running sums are gathered back into every
+// lane once, at the end of the lane's ranges.  The running maxima stay replicated (one quad
+// broadcast per chunk), since every lane rescales the accumulators of all heads.
+template <int D, int G> constexpr bool own_head_form() { return D == 128 && (G == 2 || G == 4); }
+
+// The full score of head (lane mod 4) mod G from this lane's partial dot products d[g].
+template <int G>
+__device__ __forceinline__ float reduce_own(const float (&d)[G], int q) {
+  const bool b0 = (q & 1) != 0;
+  float s;
+  if constexpr (G == 4) {
+    const bool b1 = (q & 2) != 0;
+    // keep the heads whose bit 0 is the lane's, add the partner's copy of them
+    const float k0 = (b0 ? d[1] : d[0]) + dpp_f<DPP_QUAD_XOR1>(b0 ? d[0] : d[1]);
+    const float k1 = (b0 ? d[3] : d[2]) + dpp_f<DPP_QUAD_XOR1>(b0 ? d[2] : d[3]);
+    // keep the head whose bit 1 is the lane's
+    s = (b1 ? k1 : k0) + dpp_f<DPP_QUAD_XOR2>(b1 ? k0 : k1);
+  } else {
+    s = (b0 ? d[1] : d[0]) + dpp_f<DPP_QUAD_XOR1>(b0 ? d[0] : d[1]);
+    s += dpp_f<DPP_QUAD_XOR2>(s);
+  }
+  s += dpp_f<DPP_ROW_ROR4>(s);
+  return s + dpp_f<DPP_ROW_ROR8>(s);
+}
+
+// x of lane g of the quad, for g = 0 .. G-1
+template <int G>
+__device__ __forceinline__ void quad_gather(float x, float (&out)[G]) {
+  out[0] = dpp_f<dpp_quad_bcast<0>()>(x);
+  if constexpr (G > 1) out[1] = dpp_f<dpp_quad_bcast<1>()>(x);
+  if constexpr (G > 2) out[2] = dpp_f<dpp_quad_bcast<2>()>(x);
+  if constexpr (G > 3) out[3] = dpp_f<dpp_quad_bcast<3>()>(x);
+}
 
 template <int G, typename St>
 __device__ __forceinline__ void pv_accumulate(St& S, const float (&p)[G], float w, const float (&v)[8]) {
@@ -154,6 +196,15 @@ __device__ __forceinline__ void pv_accumulate(St& S, const float (&p)[G], float 
       for (int e = 0; e < 8; ++e) PKV_ACC(S, g, e) = fmaf(pw, v[e], PKV_ACC(S, g, e));
     }
   }
+}
+
+// The own-head form of pv_accumulate: po is this lane's head's probability, which is the A
+// operand lane q % 4 of each block supplies (query heads >= G contribute 0).
+template <int G, typename St>
+__device__ __forceinline__ void pv_accumulate_own(St& S, float po, float w, const float (&v)[8], int q) {
+  const float a = (G == 4 || q < G) ? po * w : 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) S.acc4[0][e] = __builtin_amdgcn_mfma_f32_4x4x1f32(a, v[e], S.acc4[0][e], 0, 0, 0);
 }
 
 // Per-lane byte offsets of the rows a lane reads in a chunk (instruction i reads the row
@@ -230,7 +281,10 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
   bool valid[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) valid[i] = !MASKED || (tok + i * Gm::TPI < t_end);
-  float sc[NI][G];
+  constexpr bool OWN = own_head_form<D, G>();
+  const int q = threadIdx.x & 3;
+  float sc[NI][G];                   // every head's scores (OWN: unused)
+  float sco[NI];                     // OWN: this lane's head's scores
   if constexpr (KIND == CacheKind::Same || byte_kind(KIND)) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -252,13 +306,17 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
 #pragma unroll
         for (int e = 0; e < 4; ++e) d[g] = dot2<BF16>(S.qv[g][e], kw[e], d[g]);
       }
-      // stage-major across the query heads: no DPP read waits on the instruction before it
-      // (with 8 heads: long-context decode +1 %)
-      group_sum_n<LPR>(d);
       float scl = p.scale_log2;
       if constexpr (byte_kind(KIND)) scl *= R.ks[i];
+      if constexpr (OWN) {
+        sco[i] = valid[i] ? reduce_own<G>(d, q) * scl : neg_inf();
+      } else {
+        // stage-major across the query heads: no DPP read waits on the instruction before it
+        // (with 8 heads: long-context decode +1 %)
+        group_sum_n<LPR>(d);
 #pragma unroll
-      for (int g = 0; g < G; ++g) sc[i][g] = valid[i] ? d[g] * scl : neg_inf();
+        for (int g = 0; g < G; ++g) sc[i][g] = valid[i] ? d[g] * scl : neg_inf();
+      }
     }
   } else {
     // The lane's octet starts at byte (3c) mod 4 of (klo, khi); one byte permute gives
@@ -290,33 +348,48 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
 #pragma unroll
         for (int e = 0; e < 4; ++e) d[g] = dot2<BF16>(S.qv[g][e], cp[e], d[g]);
       }
-      if constexpr (G <= 4) {
-        group_sum_n<LPR>(d);
-      } else {
-#pragma unroll
-        for (int g = 0; g < G; ++g) d[g] = group_sum<LPR>(d[g]);
-      }
       const float ks = f16_lo(R.km[i]), kz = f16_hi(R.km[i]);
       const float off = BF16 ? 128.f + kz : kz;
+      if constexpr (OWN) {
+        sco[i] = valid[i] ? ks * (reduce_own<G>(d, q) - off * S.qso) * p.scale_log2 : neg_inf();
+      } else {
+        if constexpr (G <= 4) {
+          group_sum_n<LPR>(d);
+        } else {
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        // q.(code - z)*s = s * (q.code - z * sum(q))
-        sc[i][g] = valid[i] ? ks * (d[g] - off * S.qsum[g]) * p.scale_log2 : neg_inf();
+          for (int g = 0; g < G; ++g) d[g] = group_sum<LPR>(d[g]);
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          // q.(code - z)*s = s * (q.code - z * sum(q))
+          sc[i][g] = valid[i] ? ks * (d[g] - off * S.qsum[g]) * p.scale_log2 : neg_inf();
+        }
       }
     }
   }
   // Online-softmax update.  The running maxima rarely grow once a few dozen tokens have been
   // seen, so the rescaling of (l, acc) is skipped for the whole wave when no row's maximum
   // grew in this chunk: the factor would be exp2(0) = 1 exactly, so the result is the same.
-  float pp[NI][G];
+  float pp[NI][G];                   // every head's probabilities (OWN: unused)
+  float ppo[NI];                     // OWN: this lane's head's probabilities
   float mx[G];
+  float mxo = neg_inf();
   bool grow = false;
+  if constexpr (OWN) {
+    mxo = sco[0];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    mx[g] = sc[0][g];
+    for (int i = 1; i < NI; ++i) mxo = fmaxf(mxo, sco[i]);
+    quad_gather<G>(mxo, mx);
 #pragma unroll
-    for (int i = 1; i < NI; ++i) mx[g] = fmaxf(mx[g], sc[i][g]);
-    grow |= mx[g] > S.m[g];
+    for (int g = 0; g < G; ++g) grow |= mx[g] > S.m[g];
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      mx[g] = sc[0][g];
+#pragma unroll
+      for (int i = 1; i < NI; ++i) mx[g] = fmaxf(mx[g], sc[i][g]);
+      grow |= mx[g] > S.m[g];
+    }
   }
   if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
@@ -325,19 +398,38 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
       const float mu = (MASKED && mn == neg_inf()) ? 0.f : mn;   // a row with no token yet
       const float al = fast_exp2(S.m[g] - mu);
       S.m[g] = mn;
-      S.l[g] *= al;
-      if constexpr (KIND == CacheKind::U3) S.zc[g] *= al;
+      if constexpr (!OWN) {
+        S.l[g] *= al;
+        if constexpr (KIND == CacheKind::U3) S.zc[g] *= al;
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) PKV_ACC(S, g, e) *= al;
     }
+    if constexpr (OWN) {
+      const float mn = fmaxf(S.mo, mxo);
+      const float mu = (MASKED && mn == neg_inf()) ? 0.f : mn;
+      const float al = fast_exp2(S.mo - mu);
+      S.mo = mn;
+      S.lo *= al;
+      if constexpr (KIND == CacheKind::U3) S.zco *= al;
+    }
   }
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float mu = (MASKED && S.m[g] == neg_inf()) ? 0.f : S.m[g];
+  if constexpr (OWN) {
+    const float mu = (MASKED && S.mo == neg_inf()) ? 0.f : S.mo;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      pp[i][g] = fast_exp2(sc[i][g] - mu);
-      S.l[g] += pp[i][g];
+      ppo[i] = fast_exp2(sco[i] - mu);
+      S.lo += ppo[i];
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mu = (MASKED && S.m[g] == neg_inf()) ? 0.f : S.m[g];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        pp[i][g] = fast_exp2(sc[i][g] - mu);
+        S.l[g] += pp[i][g];
+      }
     }
   }
 #pragma unroll
@@ -351,7 +443,8 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
         vf[2 * e] = h_lo<BF16>(vw[e]);
         vf[2 * e + 1] = h_hi<BF16>(vw[e]);
       }
-      pv_accumulate<G>(S, pp[i], 1.f, vf);
+      if constexpr (OWN) pv_accumulate_own<G>(S, ppo[i], 1.f, vf, q);
+      else pv_accumulate<G>(S, pp[i], 1.f, vf);
     } else if constexpr (byte_kind(KIND)) {
       uint32_t vw0 = R.v[i].x, vw1 = R.v[i].y;
       float vs = R.vs[i];
@@ -361,7 +454,8 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
       codes2_to_f32<KIND, false>(vw1, vf[4], vf[5]);
       codes2_to_f32<KIND, true>(vw1, vf[6], vf[7]);
       // sum_t p (s v_t) = sum_t (p s) v_t
-      pv_accumulate<G>(S, pp[i], vs, vf);
+      if constexpr (OWN) pv_accumulate_own<G>(S, ppo[i], vs, vf, q);
+      else pv_accumulate<G>(S, pp[i], vs, vf);
     } else {
       // the same byte permute: codes 0..4 at bits 3e, codes 5..7 at bits 3e + 8
       const uint32_t y = __builtin_amdgcn_perm(R.vhi[i], R.vlo[i], (uint32_t)((3 * c) & 3) * 0x01010101u + 0x02010100u);
@@ -370,9 +464,14 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
       const float vs = valid[i] ? f16_lo(R.vm[i]) : 0.f;
       const float vz = valid[i] ? f16_hi(R.vm[i]) : 0.f;
       // sum_t p (code - z) s = sum_t (p s) code - sum_t (p s) z
+      if constexpr (OWN) {
+        S.zco = fmaf(ppo[i] * vs, vz, S.zco);
+        pv_accumulate_own<G>(S, ppo[i], vs, vf, q);
+      } else {
 #pragma unroll
-      for (int g = 0; g < G; ++g) S.zc[g] = fmaf(pp[i][g] * vs, vz, S.zc[g]);
-      pv_accumulate<G>(S, pp[i], vs, vf);
+        for (int g = 0; g < G; ++g) S.zc[g] = fmaf(pp[i][g] * vs, vz, S.zc[g]);
+        pv_accumulate<G>(S, pp[i], vs, vf);
+      }
     }
   }
 }
@@ -689,6 +788,13 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
 #pragma unroll
       for (int e = 0; e < 8; ++e) PKV_ACC(S, g, e) = 0.f;
     }
+    S.mo = neg_inf();
+    S.lo = 0.f;
+    S.zco = 0.f;
+    S.qso = S.qsum[0];
+#pragma unroll
+    for (int g = 1; g < G; ++g)
+      if ((lane & 3 & (G - 1)) == g) S.qso = S.qsum[g];
     if (seg_i > 0 && threadIdx.x < kMaxWaves) s_cnt[(seg_i + 1) & 1][threadIdx.x] = 0;
     int* cnt = &s_cnt[seg_i & 1][wv];
     auto range = [&](int ta, int tb) {
@@ -708,6 +814,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
       }
     } else {
       range(t0, t1);
+    }
+    if constexpr (own_head_form<D, G>()) {      // every head's running sums into every lane
+      quad_gather<G>(S.lo, S.l);
+      if constexpr (KIND == CacheKind::U3) quad_gather<G>(S.zco, S.zc);
     }
     merge_rows<D, G, KIND, HPI>(S);
     if (p.token_streams > 1) {
