@@ -117,7 +117,7 @@ struct State {
   float m[G], l[G], zc[G];
   // own-head form (see own_head_form): this lane's query head's running max, sum, zero-point
   // term and query sum; m, l and zc above hold every head's values again from range end on
-  float mo, lo, zco, qso;
+  float mo[2], lo[2], zco[2], qso[2];
   // accumulator column e (this lane's d = 8c + e) of query head g is acc4[g / 4][e][g % 4]: the
   // register quads are the C operands of the PV matrix-core products
   f32x4_t acc4[(G + 3) / 4][8];
@@ -135,43 +135,60 @@ struct State {
 // the long-context decode), so G = 8 keeps the FMA form.
 constexpr int kMfmaMaxG = 4;
 
-// Own-head form (2 or 4 query heads per kv head, 16 lanes per row): after the score products a
+// Own-head form (2, 4 or 8 query heads per kv head, 16 lanes per row): after the score products a
 // reduce-scatter over the quad (two DPP stages that halve the head set) and a sum over the four
 // quads of the row (two rotations) leave in lane q of every quad the full score of query head
-// q mod G, instead of every head's score in every lane.  The online softmax then runs for one
-// head per lane (a quarter of the exponentials for G = 4), the matrix-core PV takes its A
-// operand straight from that lane, and the per-head running sums are gathered back into every
-// lane once, at the end of the lane's ranges.  The running maxima stay replicated (one quad
-// broadcast per chunk), since every lane rescales the accumulators of all heads.
-template <int D, int G> constexpr bool own_head_form() { return D == 128 && (G == 2 || G == 4); }
+// q mod G (heads q and q + 4 with G = 8), instead of every head's score in every lane.  The
+// online softmax then runs for the lane's own heads only (a quarter of the exponentials), the
+// matrix-core PV takes its A operand straight from the lane, and the per-head running sums are
+// gathered back into every lane once, at the end of the lane's ranges.  The running maxima stay
+// replicated (one quad broadcast per chunk), since every lane rescales the accumulators of all
+// heads.  Measured against the replicated form: Llama-8B step 0.675 -> 0.690 of the HBM peak,
+// fp8 decode 0.434 -> 0.488, 3-bit decode 0.167 -> 0.193, long context (8 heads) 0.607 -> 0.653.
+template <int D, int G> constexpr bool own_head_form() { return D == 128 && (G == 2 || G == 4 || G == 8); }
+// heads a lane owns: q mod G (G <= 4), or q and q + 4 (G = 8)
+template <int G> constexpr int own_heads() { return G == 8 ? 2 : 1; }
 
-// The full score of head (lane mod 4) mod G from this lane's partial dot products d[g].
+// The full scores of the lane's own heads from its partial dot products d[g].
 template <int G>
-__device__ __forceinline__ float reduce_own(const float (&d)[G], int q) {
-  const bool b0 = (q & 1) != 0;
-  float s;
-  if constexpr (G == 4) {
-    const bool b1 = (q & 2) != 0;
+__device__ __forceinline__ void reduce_own(const float (&d)[G], int q, float (&s)[own_heads<G>()]) {
+  const bool b0 = (q & 1) != 0, b1 = (q & 2) != 0;
+  if constexpr (G == 8) {
+    // keep the heads whose bit 0 is the lane's (head 2j + b0), add the partner's copy of them
+    float k[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      k[j] = (b0 ? d[2 * j + 1] : d[2 * j]) + dpp_f<DPP_QUAD_XOR1>(b0 ? d[2 * j] : d[2 * j + 1]);
+    // keep the heads whose bit 1 is the lane's: q and q + 4
+    s[0] = (b1 ? k[1] : k[0]) + dpp_f<DPP_QUAD_XOR2>(b1 ? k[0] : k[1]);
+    s[1] = (b1 ? k[3] : k[2]) + dpp_f<DPP_QUAD_XOR2>(b1 ? k[2] : k[3]);
+  } else if constexpr (G == 4) {
     // keep the heads whose bit 0 is the lane's, add the partner's copy of them
     const float k0 = (b0 ? d[1] : d[0]) + dpp_f<DPP_QUAD_XOR1>(b0 ? d[0] : d[1]);
     const float k1 = (b0 ? d[3] : d[2]) + dpp_f<DPP_QUAD_XOR1>(b0 ? d[2] : d[3]);
     // keep the head whose bit 1 is the lane's
-    s = (b1 ? k1 : k0) + dpp_f<DPP_QUAD_XOR2>(b1 ? k0 : k1);
+    s[0] = (b1 ? k1 : k0) + dpp_f<DPP_QUAD_XOR2>(b1 ? k0 : k1);
   } else {
-    s = (b0 ? d[1] : d[0]) + dpp_f<DPP_QUAD_XOR1>(b0 ? d[0] : d[1]);
-    s += dpp_f<DPP_QUAD_XOR2>(s);
+    s[0] = (b0 ? d[1] : d[0]) + dpp_f<DPP_QUAD_XOR1>(b0 ? d[0] : d[1]);
+    s[0] += dpp_f<DPP_QUAD_XOR2>(s[0]);
   }
-  s += dpp_f<DPP_ROW_ROR4>(s);
-  return s + dpp_f<DPP_ROW_ROR8>(s);
+#pragma unroll
+  for (int h = 0; h < own_heads<G>(); ++h) s[h] += dpp_f<DPP_ROW_ROR4>(s[h]);
+#pragma unroll
+  for (int h = 0; h < own_heads<G>(); ++h) s[h] += dpp_f<DPP_ROW_ROR8>(s[h]);
 }
 
-// x of lane g of the quad, for g = 0 .. G-1
+// every head's value from the lanes that own it: out[g] = x[h] of lane g % 4 of the quad for
+// the own-head slot h = g / 4
 template <int G>
-__device__ __forceinline__ void quad_gather(float x, float (&out)[G]) {
-  out[0] = dpp_f<dpp_quad_bcast<0>()>(x);
-  if constexpr (G > 1) out[1] = dpp_f<dpp_quad_bcast<1>()>(x);
-  if constexpr (G > 2) out[2] = dpp_f<dpp_quad_bcast<2>()>(x);
-  if constexpr (G > 3) out[3] = dpp_f<dpp_quad_bcast<3>()>(x);
+__device__ __forceinline__ void quad_gather(const float* x, float (&out)[G]) {
+#pragma unroll
+  for (int h = 0; h < own_heads<G>(); ++h) {
+    out[4 * h] = dpp_f<dpp_quad_bcast<0>()>(x[h]);
+    if constexpr (G > 1) out[4 * h + 1] = dpp_f<dpp_quad_bcast<1>()>(x[h]);
+    if constexpr (G > 2) out[4 * h + 2] = dpp_f<dpp_quad_bcast<2>()>(x[h]);
+    if constexpr (G > 3) out[4 * h + 3] = dpp_f<dpp_quad_bcast<3>()>(x[h]);
+  }
 }
 
 template <int G, typename St>
@@ -200,11 +217,20 @@ __device__ __forceinline__ void pv_accumulate(St& S, const float (&p)[G], float 
 
 // The own-head form of pv_accumulate: po is this lane's head's probability, which is the A
 // operand lane q % 4 of each block supplies (query heads >= G contribute 0).
+// With 8 heads the matrix-core form spills, so the probabilities are gathered into every lane
+// (two quad broadcasts per head set) and the FMA form of pv_accumulate is kept.
 template <int G, typename St>
-__device__ __forceinline__ void pv_accumulate_own(St& S, float po, float w, const float (&v)[8], int q) {
-  const float a = (G == 4 || q < G) ? po * w : 0.f;
+__device__ __forceinline__ void pv_accumulate_own(St& S, const float (&po)[own_heads<G>()], float w,
+                                                  const float (&v)[8], int q) {
+  if constexpr (G <= kMfmaMaxG) {
+    const float a = (G == 4 || q < G) ? po[0] * w : 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) S.acc4[0][e] = __builtin_amdgcn_mfma_f32_4x4x1f32(a, v[e], S.acc4[0][e], 0, 0, 0);
+    for (int e = 0; e < 8; ++e) S.acc4[0][e] = __builtin_amdgcn_mfma_f32_4x4x1f32(a, v[e], S.acc4[0][e], 0, 0, 0);
+  } else {
+    float pg[G];
+    quad_gather<G>(po, pg);
+    pv_accumulate<G>(S, pg, w, v);
+  }
 }
 
 // Per-lane byte offsets of the rows a lane reads in a chunk (instruction i reads the row
@@ -284,7 +310,8 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
   constexpr bool OWN = own_head_form<D, G>();
   const int q = threadIdx.x & 3;
   float sc[NI][G];                   // every head's scores (OWN: unused)
-  float sco[NI];                     // OWN: this lane's head's scores
+  constexpr int HO = own_heads<G>();
+  float sco[NI][HO];                 // OWN: this lane's heads' scores
   if constexpr (KIND == CacheKind::Same || byte_kind(KIND)) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -309,7 +336,10 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
       float scl = p.scale_log2;
       if constexpr (byte_kind(KIND)) scl *= R.ks[i];
       if constexpr (OWN) {
-        sco[i] = valid[i] ? reduce_own<G>(d, q) * scl : neg_inf();
+        float so[HO];
+        reduce_own<G>(d, q, so);
+#pragma unroll
+        for (int h = 0; h < HO; ++h) sco[i][h] = valid[i] ? so[h] * scl : neg_inf();
       } else {
         // stage-major across the query heads: no DPP read waits on the instruction before it
         // (with 8 heads: long-context decode +1 %)
@@ -351,7 +381,11 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
       const float ks = f16_lo(R.km[i]), kz = f16_hi(R.km[i]);
       const float off = BF16 ? 128.f + kz : kz;
       if constexpr (OWN) {
-        sco[i] = valid[i] ? ks * (reduce_own<G>(d, q) - off * S.qso) * p.scale_log2 : neg_inf();
+        float so[HO];
+        reduce_own<G>(d, q, so);
+#pragma unroll
+        for (int h = 0; h < HO; ++h)
+          sco[i][h] = valid[i] ? ks * (so[h] - off * S.qso[h]) * p.scale_log2 : neg_inf();
       } else {
         if constexpr (G <= 4) {
           group_sum_n<LPR>(d);
@@ -371,14 +405,17 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
   // seen, so the rescaling of (l, acc) is skipped for the whole wave when no row's maximum
   // grew in this chunk: the factor would be exp2(0) = 1 exactly, so the result is the same.
   float pp[NI][G];                   // every head's probabilities (OWN: unused)
-  float ppo[NI];                     // OWN: this lane's head's probabilities
+  float ppo[NI][HO];                 // OWN: this lane's heads' probabilities
   float mx[G];
-  float mxo = neg_inf();
+  float mxo[HO];
   bool grow = false;
   if constexpr (OWN) {
-    mxo = sco[0];
 #pragma unroll
-    for (int i = 1; i < NI; ++i) mxo = fmaxf(mxo, sco[i]);
+    for (int h = 0; h < HO; ++h) {
+      mxo[h] = sco[0][h];
+#pragma unroll
+      for (int i = 1; i < NI; ++i) mxo[h] = fmaxf(mxo[h], sco[i][h]);
+    }
     quad_gather<G>(mxo, mx);
 #pragma unroll
     for (int g = 0; g < G; ++g) grow |= mx[g] > S.m[g];
@@ -406,20 +443,26 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
       for (int e = 0; e < 8; ++e) PKV_ACC(S, g, e) *= al;
     }
     if constexpr (OWN) {
-      const float mn = fmaxf(S.mo, mxo);
-      const float mu = (MASKED && mn == neg_inf()) ? 0.f : mn;
-      const float al = fast_exp2(S.mo - mu);
-      S.mo = mn;
-      S.lo *= al;
-      if constexpr (KIND == CacheKind::U3) S.zco *= al;
+#pragma unroll
+      for (int h = 0; h < HO; ++h) {
+        const float mn = fmaxf(S.mo[h], mxo[h]);
+        const float mu = (MASKED && mn == neg_inf()) ? 0.f : mn;
+        const float al = fast_exp2(S.mo[h] - mu);
+        S.mo[h] = mn;
+        S.lo[h] *= al;
+        if constexpr (KIND == CacheKind::U3) S.zco[h] *= al;
+      }
     }
   }
   if constexpr (OWN) {
-    const float mu = (MASKED && S.mo == neg_inf()) ? 0.f : S.mo;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      ppo[i] = fast_exp2(sco[i] - mu);
-      S.lo += ppo[i];
+    for (int h = 0; h < HO; ++h) {
+      const float mu = (MASKED && S.mo[h] == neg_inf()) ? 0.f : S.mo[h];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        ppo[i][h] = fast_exp2(sco[i][h] - mu);
+        S.lo[h] += ppo[i][h];
+      }
     }
   } else {
 #pragma unroll
@@ -465,7 +508,8 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
       const float vz = valid[i] ? f16_hi(R.vm[i]) : 0.f;
       // sum_t p (code - z) s = sum_t (p s) code - sum_t (p s) z
       if constexpr (OWN) {
-        S.zco = fmaf(ppo[i] * vs, vz, S.zco);
+#pragma unroll
+        for (int h = 0; h < HO; ++h) S.zco[h] = fmaf(ppo[i][h] * vs, vz, S.zco[h]);
         pv_accumulate_own<G>(S, ppo[i], vs, vf, q);
       } else {
 #pragma unroll
@@ -788,13 +832,18 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
 #pragma unroll
       for (int e = 0; e < 8; ++e) PKV_ACC(S, g, e) = 0.f;
     }
-    S.mo = neg_inf();
-    S.lo = 0.f;
-    S.zco = 0.f;
-    S.qso = S.qsum[0];
 #pragma unroll
-    for (int g = 1; g < G; ++g)
-      if ((lane & 3 & (G - 1)) == g) S.qso = S.qsum[g];
+    for (int h = 0; h < 2; ++h) {
+      S.mo[h] = neg_inf();
+      S.lo[h] = 0.f;
+      S.zco[h] = 0.f;
+      // the query sums of the lane's own heads (q mod G, or q and q + 4 with 8 heads)
+      const int own = (G == 8) ? (lane & 3) + 4 * h : (lane & 3 & (G - 1));
+      S.qso[h] = S.qsum[0];
+#pragma unroll
+      for (int g = 1; g < G; ++g)
+        if (own == g) S.qso[h] = S.qsum[g];
+    }
     if (seg_i > 0 && threadIdx.x < kMaxWaves) s_cnt[(seg_i + 1) & 1][threadIdx.x] = 0;
     int* cnt = &s_cnt[seg_i & 1][wv];
     auto range = [&](int ta, int tb) {
