@@ -157,7 +157,7 @@ int kv_append_scaled(const void* k_new, const void* v_new, pkv_dtype in_dtype,
  * granule) units sized to its expected speed, where a granule is `partition_size` tokens;
  * a context is cut at multiples of the granule, except that where a block of the cache
  * holds at least 64 KB of a wave's K/V the workgroups sharing a context hand its blocks out
- * among themselves at run time, in pieces of up to 32 tokens.  The workspace holds the partial states of the ranges that get
+ * among themselves at run time, a block at a time.  The workspace holds the partial states of the ranges that get
  * cut, so its size depends on the current device's compute-unit count: query it on the
  * device that will run the call.
  * partition_size: 0 = automatic (16 tokens, the finest balance), else a multiple of 16.

@@ -73,10 +73,11 @@ constexpr SplitWeights kSplitStaticU3{96, 96, 64, 64};
 constexpr SplitWeights kSplitClaimed{88, 88, 64, 64};
 // run-time hand-out of shared segments: from this many bytes of K/V per wave and block, in
 // units of this many chunks (0: whole blocks).  Measured on the long-context decode (64-token
-// blocks, 4-token chunks): 8-chunk units +1 % against whole blocks; 4-chunk units 30 % slower,
-// each claim is a device-scope atomic on a counter that every sharer uses.
+// blocks, 4-token chunks): with the own-head decode form whole blocks are 2.5 % faster than
+// 8-chunk units (with the replicated form 8-chunk units had been 1 % faster); 4-chunk units are
+// 30 % slower: each claim is a device-scope atomic on a counter that every sharer uses.
 constexpr int64_t kClaimMinBlockBytes = 64 * 1024;
-constexpr int kClaimUnitChunks = 8;
+constexpr int kClaimUnitChunks = 0;
 // a workgroup that starts a segment inside its range first waits for the segment's context
 // length, q and block table: charged to the static split as this many tokens of work
 // (measured with one 8-wave workgroup per CU: 16 -> 48 gains 1 % on the Llama-8B step, 2 % on
