@@ -135,22 +135,24 @@ struct State {
 // the long-context decode), so G = 8 keeps the FMA form.
 constexpr int kMfmaMaxG = 4;
 
-// Own-head form (2, 4 or 8 query heads per kv head, 16 lanes per row): after the score products a
-// reduce-scatter over the quad (two DPP stages that halve the head set) and a sum over the four
-// quads of the row (two rotations) leave in lane q of every quad the full score of query head
-// q mod G (heads q and q + 4 with G = 8), instead of every head's score in every lane.  The
-// online softmax then runs for the lane's own heads only (a quarter of the exponentials), the
-// matrix-core PV takes its A operand straight from the lane, and the per-head running sums are
-// gathered back into every lane once, at the end of the lane's ranges.  The running maxima stay
-// replicated (one quad broadcast per chunk), since every lane rescales the accumulators of all
-// heads.  Measured against the replicated form: Llama-8B step 0.675 -> 0.690 of the HBM peak,
-// fp8 decode 0.434 -> 0.488, 3-bit decode 0.167 -> 0.193, long context (8 heads) 0.607 -> 0.653.
-template <int D, int G> constexpr bool own_head_form() { return D == 128 && (G == 2 || G == 4 || G == 8); }
+// Own-head form (2, 4 or 8 query heads per kv head): after the score products a reduce-scatter
+// over the quad (two DPP stages that halve the head set) and a sum over the quads of the row
+// (two rotations for 16-lane rows, one lane permute for 8-lane rows) leave in lane q of every
+// quad the full score of query head q mod G (heads q and q + 4 with G = 8), instead of every
+// head's score in every lane.  The online softmax then runs for the lane's own heads only (a
+// quarter of the exponentials), the matrix-core PV takes its A operand straight from the lane,
+// and the per-head running sums are gathered back into every lane once, at the end of the
+// lane's ranges.  The running maxima stay replicated (one quad broadcast per chunk), since every
+// lane rescales the accumulators of all heads.  Measured against the replicated form: Llama-8B
+// step 0.675 -> 0.690 of the HBM peak, fp8 decode 0.434 -> 0.488, 3-bit decode 0.167 -> 0.193,
+// long context (8 heads) 0.607 -> 0.653; head_dim 64, 4 / 8 heads: 0.580 -> 0.593, 0.42 -> 0.44.
+template <int D, int G> constexpr bool own_head_form() { return G == 2 || G == 4 || G == 8; }
 // heads a lane owns: q mod G (G <= 4), or q and q + 4 (G = 8)
 template <int G> constexpr int own_heads() { return G == 8 ? 2 : 1; }
 
-// The full scores of the lane's own heads from its partial dot products d[g].
-template <int G>
+// The full scores of the lane's own heads from its partial dot products d[g], for rows of LPR
+// lanes (16: D = 128; 8: D = 64).
+template <int G, int LPR>
 __device__ __forceinline__ void reduce_own(const float (&d)[G], int q, float (&s)[own_heads<G>()]) {
   const bool b0 = (q & 1) != 0, b1 = (q & 2) != 0;
   if constexpr (G == 8) {
@@ -172,10 +174,17 @@ __device__ __forceinline__ void reduce_own(const float (&d)[G], int q, float (&s
     s[0] = (b0 ? d[1] : d[0]) + dpp_f<DPP_QUAD_XOR1>(b0 ? d[0] : d[1]);
     s[0] += dpp_f<DPP_QUAD_XOR2>(s[0]);
   }
+  if constexpr (LPR == 16) {
+    // the four quads of the row: rotations by 4 and 8 keep a lane's place in its quad
 #pragma unroll
-  for (int h = 0; h < own_heads<G>(); ++h) s[h] += dpp_f<DPP_ROW_ROR4>(s[h]);
+    for (int h = 0; h < own_heads<G>(); ++h) s[h] += dpp_f<DPP_ROW_ROR4>(s[h]);
 #pragma unroll
-  for (int h = 0; h < own_heads<G>(); ++h) s[h] += dpp_f<DPP_ROW_ROR8>(s[h]);
+    for (int h = 0; h < own_heads<G>(); ++h) s[h] += dpp_f<DPP_ROW_ROR8>(s[h]);
+  } else {
+    // the two quads of an 8-lane row: lane i and lane i ^ 4 (a cross-lane permute)
+#pragma unroll
+    for (int h = 0; h < own_heads<G>(); ++h) s[h] += __shfl_xor(s[h], 4);
+  }
 }
 
 // every head's value from the lanes that own it: out[g] = x[h] of lane g % 4 of the quad for
@@ -337,7 +346,7 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
       if constexpr (byte_kind(KIND)) scl *= R.ks[i];
       if constexpr (OWN) {
         float so[HO];
-        reduce_own<G>(d, q, so);
+        reduce_own<G, LPR>(d, q, so);
 #pragma unroll
         for (int h = 0; h < HO; ++h) sco[i][h] = valid[i] ? so[h] * scl : neg_inf();
       } else {
@@ -382,7 +391,7 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
       const float off = BF16 ? 128.f + kz : kz;
       if constexpr (OWN) {
         float so[HO];
-        reduce_own<G>(d, q, so);
+        reduce_own<G, LPR>(d, q, so);
 #pragma unroll
         for (int h = 0; h < HO; ++h)
           sco[i][h] = valid[i] ? ks * (so[h] - off * S.qso[h]) * p.scale_log2 : neg_inf();
