@@ -197,13 +197,13 @@ size_t paged_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads,
  *   partition_size   split granule in tokens (0 = automatic; else a multiple of 16); see
  *                    paged_decode_workspace_size.
  *   workspace        device, >= paged_decode_workspace_size(...) bytes, 256-byte aligned,
- *                    zero-filled once before its first use.  Its first 256 KB hold counters
- *                    through which the workgroups sharing a (request, head group) hand out its
- *                    blocks at run time; every call leaves them at zero again and overwrites
- *                    all else it reads, so one workspace serves calls of every shape it is
- *                    large enough for.  (Contents that are not zero there make a call lose
- *                    work, not fault.)  One workspace per stream: calls sharing it must be
- *                    ordered.
+ *                    with any contents: a call reads nothing from it that the same call did
+ *                    not write first (the counters through which the workgroups sharing a
+ *                    (request, head group) hand out its blocks at run time are cleared by a
+ *                    kernel of the call, ahead of the decode), so a fresh uninitialised
+ *                    allocation is fine and one workspace serves calls of every shape it is
+ *                    large enough for.  Calls sharing a workspace must be ordered (same
+ *                    stream, or synchronised); overlapping calls on it race.
  *   batch            0 .. 8192.
  * Accumulation is fp32; outputs are rounded to q_dtype to nearest even.
  */

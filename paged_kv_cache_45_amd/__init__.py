@@ -179,13 +179,14 @@ def paged_decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int,
 
 def decode_workspace(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                      max_context_len: int, partition_size: int = 0, device="cuda"):
-    """Allocate the (zero-filled) workspace paged_decode needs on `device` (None if none)."""
+    """Allocate the workspace paged_decode needs on `device` (None if none).  Its contents do
+    not matter: every call writes what it reads."""
     import torch
     n = paged_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_context_len,
                                     partition_size)
     if n == 0:
         return None
-    return torch.zeros(n, dtype=torch.uint8, device=device)
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def paged_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,

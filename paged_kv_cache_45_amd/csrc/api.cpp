@@ -83,17 +83,19 @@ constexpr int kClaimUnitChunks = 0;
 // (measured with one 8-wave workgroup per CU: 16 -> 48 gains 1 % on the Llama-8B step, 2 % on
 // the 3-bit decode; 32 and 48 are equal on the former)
 constexpr int kSegmentStartTokens = 48;
-// Block counters kept at the head of every decode workspace (4 per (request, kv-head group)
-// segment); calls with more segments use the static split only.
-constexpr size_t kClaimSlots = 65536;
+// block hand-out counters per (request, kv-head group) segment: one per head wave
+constexpr size_t kClaimCounters = 4;
 
 struct DecodeLayout {
   pkv::DecodePlan plan;
   size_t claim_off, acc_off, ml_off, seg_off, bytes;
 };
 
-// Workspace layout of paged_decode: partial accumulators, partial (m, l), and per segment
-// (request, kv-head group) the slot of its first partial and the owner of its last unit.
+// Workspace layout of paged_decode: the block hand-out counters (kClaimCounters per segment), the
+// partial accumulators, the partial (m, l), and per segment (request, kv-head group) the slot of
+// its first partial and the owner of its last unit.  Every call writes each part before it reads
+// it (the counters through the clearing kernel ahead of the decode), so the workspace needs no
+// particular contents and one workspace serves calls of every shape it is large enough for.
 DecodeLayout decode_layout(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                            int max_context_len, int ps, int bf16, int kind) {
   DecodeLayout L{};
@@ -101,11 +103,9 @@ DecodeLayout decode_layout(int batch, int num_q_heads, int num_kv_heads, int hea
   L.plan = pkv::plan_decode(batch, num_q_heads, num_kv_heads, head_dim, max_context_len, ps, bf16, kind);
   const size_t slots = (size_t)L.plan.num_wgs * 2 * L.plan.heads_per_group * group;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  // The block counters come first, at a fixed size: they must be zero when a call starts, and a
-  // region whose place does not depend on the call's shape keeps them apart from the partials
-  // that an earlier call of another shape wrote into the same workspace.
+  const size_t segs = (size_t)batch * L.plan.num_head_groups;
   L.claim_off = 0;
-  L.acc_off = kClaimSlots * sizeof(int);
+  L.acc_off = up(segs * kClaimCounters * sizeof(int));
   L.ml_off = L.acc_off + up(slots * head_dim * sizeof(float));
   L.seg_off = L.ml_off + up(slots * 2 * sizeof(float));
   L.bytes = L.seg_off + up((size_t)batch * L.plan.num_head_groups * 2 * sizeof(int));
@@ -408,8 +408,7 @@ static int decode_impl(void* out, const void* q, pkv_dtype q_dtype,
   const int unit_tokens = kClaimUnitChunks > 0 ? std::min(block_size, kClaimUnitChunks * L.plan.chunk_tokens)
                                                : block_size;
   p.claim_units = (wave_block_bytes >= kClaimMinBlockBytes && unit_tokens % (L.plan.chunk_tokens * 2) == 0 &&
-                   L.plan.heads_per_group / L.plan.hpi <= 4 &&
-                   (size_t)batch * L.plan.num_head_groups * 4 <= kClaimSlots) ? 1 : 0;
+                   L.plan.heads_per_group / L.plan.hpi <= kClaimCounters) ? 1 : 0;
   p.log2_claim = 0;
   while ((1 << p.log2_claim) < unit_tokens) ++p.log2_claim;
   const SplitWeights sw = p.claim_units ? kSplitClaimed : cache_dtype == PKV_U3 ? kSplitStaticU3 : kSplitStatic;

@@ -23,9 +23,6 @@ __global__ __launch_bounds__(D * kMergeMaxSplit) void merge_kernel(DecodeParams 
   const int hg = kvh / p.heads_per_group, hh = kvh % p.heads_per_group;
   const int d = threadIdx.x % D, part = threadIdx.x / D;
   uint16_t* out = static_cast<uint16_t*>(p.out) + b * p.o_sb + (int64_t)(kvh * G + g) * p.o_sh;
-  // the decode kernel has finished: leave the segment's block counters at zero for the next call
-  if (p.claim_units && hh == 0 && g == 0 && threadIdx.x < kClaimWaves)
-    p.ws_claim[((int64_t)b * p.num_head_groups + hg) * kClaimWaves + threadIdx.x] = 0;
   // The decode kernel recorded, for this (request, head group) segment, the partial slot of the
   // workgroup w0 that holds its first unit (2 * w0 + 0 if the segment starts w0's range, else
   // 2 * w0 + 1) and the workgroup w1 that holds its last unit; w0 + 1 .. w1 keep theirs in
@@ -87,6 +84,16 @@ __global__ __launch_bounds__(D * kMergeMaxSplit) void merge_kernel(DecodeParams 
     const float o = At / Lt;
     out[d] = (uint16_t)(BF16 ? f32_to_bf16_bits(o) : f32_to_f16_bits(o));
   }
+}
+
+// The run-time block hand-out counts the claims of each shared (request, head group) segment
+// from zero.  Its counters (kClaimWaves per segment, at the head of the workspace) are cleared by
+// this kernel ahead of the decode kernel of the same call, so a call reads nothing from the
+// workspace that it did not write itself: any earlier contents (a fresh allocation, another
+// shape's partials, a call whose later launch failed) give the same result.  A kernel, not a
+// memset, so that a captured call records no memset node.
+__global__ __launch_bounds__(256) void claim_clear_kernel(int* counters, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) counters[i] = 0;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -188,8 +195,17 @@ hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan, CacheKin
   const void* mf = merge_kernel_ptr(head_dim, group, bf16);
   if (!fn || !mf) return hipErrorInvalidValue;
   void* args[] = {const_cast<DecodeParams*>(&p)};
-  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)plan.num_wgs), dim3(plan.waves_per_wg * 64), args,
-                                 plan.lds_bytes, s);
+  hipError_t e = hipSuccess;
+  if (p.claim_units) {
+    int* counters = p.ws_claim;
+    int n = (int)((int64_t)p.batch * plan.num_head_groups * kClaimWaves);
+    void* cargs[] = {&counters, &n};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&claim_clear_kernel),
+                        dim3((unsigned)std::min(64, (n + 255) / 256)), dim3(256), cargs, 0, s);
+    if (e != hipSuccess) return e;
+  }
+  e = hipLaunchKernel(fn, dim3((unsigned)plan.num_wgs), dim3(plan.waves_per_wg * 64), args,
+                      plan.lds_bytes, s);
   if (e != hipSuccess) return e;
   // split the partials of a segment so that each thread merges about 2 x kMergeBatch of them
   const int64_t per_seg = plan.num_wgs / std::max<int64_t>(1, (int64_t)p.batch * plan.num_head_groups) + 2;

@@ -175,11 +175,16 @@ __device__ __forceinline__ void reduce_own(const float (&d)[G], int q, float (&s
     s[0] += dpp_f<DPP_QUAD_XOR2>(s[0]);
   }
   if constexpr (LPR == 16) {
-    // the four quads of the row: rotations by 4 and 8 keep a lane's place in its quad
-#pragma unroll
-    for (int h = 0; h < own_heads<G>(); ++h) s[h] += dpp_f<DPP_ROW_ROR4>(s[h]);
+    // the four quads of the row: rotations by 8 and then 4 keep a lane's place in its quad.  In
+    // this order every quad adds the same pairs, (s0 + s2) + (s1 + s3) up to the order of the
+    // operands of each addition, so all four quads hold bit-identical scores, and the row's
+    // running maxima and sums (taken from its first quad where one value per row is written)
+    // are those its accumulators were built with.  (Rotating by 4 first pairs the quads
+    // differently in different quads.)
 #pragma unroll
     for (int h = 0; h < own_heads<G>(); ++h) s[h] += dpp_f<DPP_ROW_ROR8>(s[h]);
+#pragma unroll
+    for (int h = 0; h < own_heads<G>(); ++h) s[h] += dpp_f<DPP_ROW_ROR4>(s[h]);
   } else {
     // the two quads of an 8-lane row: lane i and lane i ^ 4 (a cross-lane permute)
 #pragma unroll
@@ -631,8 +636,8 @@ __device__ __forceinline__ void run_claimed(const DecodeParams& p, State<G>& S, 
   const char* vc = static_cast<const char*>(p.v_cache) + (int64_t)h_first * p.c_sh * esz;
   const char* kmc = static_cast<const char*>(p.k_meta) + (int64_t)h_first * p.m_sh * 4;
   const char* vmc = static_cast<const char*>(p.v_meta) + (int64_t)h_first * p.m_sh * 4;
-  // a claim outside [0, nu) ends the loop: a counter that is not zero at the start of the call
-  // (a workspace that was not zero-filled) can only lose work, never read outside the segment
+  // the counters are cleared by a kernel ahead of this one in the same call; a claim outside
+  // [0, nu) ends the loop, so no claim can read outside the segment
   auto take = [&](int v) { return (unsigned)v < (unsigned)nu ? v : nu; };
   typedef __attribute__((address_space(1))) int GlobalInt;
   GlobalInt* const claim_g = (GlobalInt*)claim;          // a global atomic (vmcnt only)

@@ -226,9 +226,9 @@ def test_rejects_bad_arguments():
 
 
 def test_workspace_reused_across_calls():
-    """One zero-filled workspace serves consecutive calls of different batch sizes and partition
-    sizes: the block counters that the sharing workgroups claim from are left at zero by every
-    call, and each call overwrites every partial state and segment record it reads."""
+    """One workspace serves consecutive calls of different batch sizes and partition sizes: each
+    call clears the block counters it claims from and overwrites every partial state and segment
+    record it reads."""
     P = need_gpu()
     big = W.llama8b_decode("cuda", batch=48, seed=W.BASE_SEED + 21)
     small = W.llama8b_decode("cuda", batch=5, seed=W.BASE_SEED + 22)
@@ -259,6 +259,36 @@ def test_block_claiming_ragged():
     for rep in range(3):                  # the same workspace: the counters restart at zero
         out = _decode(P, wl, wl.k_pool, wl.v_pool, wl.ctx_after, workspace=ws)
         assert report(f"claims rep {rep}", f32_of(out), want, wl.dtype) <= ATTN_TOL
+
+
+@pytest.mark.parametrize("fill", ["small-counts", "ones", "random"])
+def test_workspace_any_contents(fill):
+    """The workspace may hold anything when a call starts.  The block hand-out counters are the
+    part a call would otherwise read before writing: filled with small counts inside the claim
+    range (the case that would skip blocks silently), all-ones bytes or random bytes, the
+    claimed long-context path matches the oracle at partition sizes 16 and 512, on every one of
+    three calls."""
+    P = need_gpu()
+    lens = [1, 63, 64, 65, 5000, 20011, 129, 12345]
+    wl = W.decode_workload("claims-dirty", batch=len(lens), num_q_heads=32, num_kv_heads=8,
+                           head_dim=128, block_size=64, ctx_lo=0, ctx_hi=0, dtype=torch.bfloat16,
+                           device="cuda", seed=W.BASE_SEED + 32, append_one=False, ctx_override=lens)
+    want = _oracle_same(wl, wl.k_pool, wl.v_pool, wl.ctx_after)
+    for ps in (0, 512):
+        n = P.paged_decode_workspace_size(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                          max(lens), ps)
+        ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+        gen = torch.Generator(device="cuda").manual_seed(7)
+        for rep in range(3):
+            if fill == "small-counts":
+                ws.view(torch.int32)[: n // 4 // 2].fill_(rep + 1)
+            elif fill == "ones":
+                ws.fill_(0xFF)
+            else:
+                ws.copy_(torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda", generator=gen))
+            out = _decode(P, wl, wl.k_pool, wl.v_pool, wl.ctx_after, partition_size=ps, workspace=ws)
+            assert report(f"dirty workspace {fill} ps={ps} rep {rep}", f32_of(out), want,
+                          wl.dtype) <= ATTN_TOL
 
 
 # ---- fp8 e4m3fn cache (one fp32 scale per (slot, kv head)) ---------------------------------
