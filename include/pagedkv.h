@@ -46,7 +46,8 @@ typedef enum {
   PKV_EINVAL = -1,
   PKV_EUNSUPPORTED = -2,
   PKV_EWORKSPACE = -3,
-  PKV_EHIP = -4
+  PKV_EHIP = -4,
+  PKV_ESCRATCH = -5    /* paged_decode_noalloc: the call needs more than its static scratch */
 } pkv_status;
 
 typedef enum {
@@ -241,6 +242,31 @@ int paged_decode_scaled(void* out, const void* q, pkv_dtype q_dtype,
                         int batch, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                         int64_t num_blocks, int max_context_len, float sm_scale, int partition_size,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * paged_decode_noalloc - paged_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * Arguments, validation, kernels and results as for paged_decode, without workspace arguments:
+ * the partial states go to a static device array of 24 MiB that the library holds on each GPU
+ * it runs on until the process ends (its device address is looked up on the first call on each
+ * device).  The call allocates and frees nothing.  Limit: a call whose workspace
+ * (paged_decode_workspace_size of its shape, on this device) exceeds 24 MiB returns
+ * PKV_ESCRATCH and writes nothing; on a 256-CU MI355X the long-context shape (batch 8, 64 / 8
+ * heads, head_dim 128) needs about 16.3 MiB and the Llama-8B decode shape about 8.5 MiB.  Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (different streams without ordering, or
+ * several threads) race and give undefined results; ordered calls are independent (each call
+ * writes what it reads).
+ */
+int paged_decode_noalloc(void* out, const void* q, pkv_dtype q_dtype,
+                         int64_t q_stride_b, int64_t q_stride_h, int64_t o_stride_b, int64_t o_stride_h,
+                         const void* k_cache, const void* v_cache, pkv_dtype cache_dtype,
+                         int64_t c_stride_block, int64_t c_stride_slot, int64_t c_stride_head,
+                         const void* k_meta, const void* v_meta,
+                         const int32_t* block_tables, int64_t bt_stride_b, const int32_t* context_lens,
+                         int batch, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                         int64_t num_blocks, int max_context_len, float sm_scale, int partition_size,
+                         hipStream_t stream);
 
 /*
  * build_slot_mapping - the slot id of every new token from its request and position.

@@ -7,7 +7,7 @@ in the HIP kernels.  There is no fallback: if the library is missing or a call f
 an exception is raised.
 
 Entry points (same names as the C ABI):
-    kv_append, kv_append_scaled, paged_decode, paged_decode_scaled,
+    kv_append, kv_append_scaled, paged_decode, paged_decode_scaled, paged_decode_noalloc,
     paged_decode_workspace_size, build_slot_mapping, pack3, unpack3, pkv_status_string
 """
 from __future__ import annotations
@@ -17,14 +17,15 @@ import math
 import os
 from typing import Optional
 
-__all__ = ["kv_append", "kv_append_scaled", "paged_decode", "paged_decode_scaled", "build_slot_mapping", "paged_decode_workspace_size", "pack3", "unpack3",
+__all__ = ["kv_append", "kv_append_scaled", "paged_decode", "paged_decode_scaled", "paged_decode_noalloc",
+           "build_slot_mapping", "paged_decode_workspace_size", "pack3", "unpack3",
            "pkv_status_string", "decode_workspace", "library_path", "load_library",
            "PKV_F16", "PKV_BF16", "PKV_FP8_E4M3FN", "PKV_U3", "PKV_FP8_E5M2", "PKV_INT8",
            "PagedKVError"]
 
 PKV_F16, PKV_BF16, PKV_FP8_E4M3FN, PKV_U3, PKV_FP8_E5M2, PKV_INT8 = 0, 1, 2, 3, 4, 5
 _STATUS = {0: "PKV_OK", -1: "PKV_EINVAL", -2: "PKV_EUNSUPPORTED", -3: "PKV_EWORKSPACE",
-           -4: "PKV_EHIP"}
+           -4: "PKV_EHIP", -5: "PKV_ESCRATCH"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -68,6 +69,10 @@ def load_library() -> ctypes.CDLL:
     lib.paged_decode_scaled.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, vp, i32, i64, i64, i64,
                                         vp, vp, i64, i64, i64, vp, i64, vp, i32, i32, i32, i32, i32,
                                         i64, i32, f32, i32, vp, sz, vp]
+    lib.paged_decode_noalloc.restype = i32
+    lib.paged_decode_noalloc.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, vp, i32, i64, i64, i64,
+                                         vp, vp, vp, i64, vp, i32, i32, i32, i32, i32, i64, i32, f32,
+                                         i32, vp]
     lib.build_slot_mapping.restype = i32
     lib.build_slot_mapping.argtypes = [vp, vp, i64, vp, i64, i32, i32, vp, vp]
     lib.pack3.restype = i32
@@ -225,6 +230,35 @@ def paged_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_le
     else:
         st = load_library().paged_decode(*head, *tail)
         _check("paged_decode", st)
+    return out
+
+
+def paged_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
+                         sm_scale: Optional[float] = None, k_meta=None, v_meta=None,
+                         partition_size: int = 0, out=None, cache_dtype=None, stream=None):
+    """paged_decode with the library's static device scratch in place of a workspace (the
+    library allocates nothing; the caller passes q, the caches and out).  Calls that overlap on
+    one GPU share the scratch and race."""
+    import torch
+    qdt = _dtype16(q)
+    if q.dim() != 3 or q.stride(2) != 1:
+        raise ValueError("q must be [B, Hq, D] with unit stride on D")
+    B, Hq, D = q.shape
+    cdt = _cache_dtype(k_cache, qdt, cache_dtype)
+    sb, ss, sh = _cache_strides(k_cache, v_cache)
+    if out is None:
+        out = torch.empty_like(q)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    if block_tables.dim() != 2 or block_tables.stride(1) != 1:
+        raise ValueError("block_tables must be [B, max_blocks] with unit stride")
+    st = load_library().paged_decode_noalloc(
+        _ptr(out), _ptr(q), qdt, q.stride(0), q.stride(1), out.stride(0), out.stride(1),
+        _ptr(k_cache), _ptr(v_cache), cdt, sb, ss, sh, _ptr(k_meta), _ptr(v_meta),
+        _ptr(block_tables), block_tables.stride(0), _ptr(context_lens), B, Hq, k_cache.shape[2], D,
+        k_cache.shape[1], k_cache.shape[0], int(max_context_len), float(sm_scale),
+        int(partition_size), _stream(stream))
+    _check("paged_decode_noalloc", st)
     return out
 
 

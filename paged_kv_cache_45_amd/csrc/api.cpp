@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstddef>
+#include <mutex>
 
 #include "../../include/pagedkv.h"
 #include "launch.h"
@@ -123,6 +124,7 @@ const char* pkv_status_string(int status) {
     case PKV_EUNSUPPORTED: return "unsupported configuration";
     case PKV_EWORKSPACE: return "workspace missing or too small";
     case PKV_EHIP: return "HIP launch failed";
+    case PKV_ESCRATCH: return "the call needs more decode scratch than the static buffer holds";
     default: return "unknown status";
   }
 }
@@ -457,3 +459,56 @@ int paged_decode_scaled(void* out, const void* q, pkv_dtype q_dtype,
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// paged_decode_noalloc: paged_decode with its workspace in a file-scope device array, for callers
+// that cannot allocate.  `scratch` is a host-side stand-in for the array in host code; its device
+// address, which differs per GPU, comes from hipGetSymbolAddress on each device's first call and
+// is the only form in which host code passes the array on.
+// ---------------------------------------------------------------------------------------------
+namespace {
+constexpr size_t kScratchBytes = size_t(24) << 20;          // 24 MiB per GPU
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (looked up once per device, with that device current).
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PKV_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return PKV_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return PKV_EHIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+}  // namespace
+
+extern "C" int paged_decode_noalloc(void* out, const void* q, pkv_dtype q_dtype,
+                                    int64_t q_stride_b, int64_t q_stride_h, int64_t o_stride_b,
+                                    int64_t o_stride_h, const void* k_cache, const void* v_cache,
+                                    pkv_dtype cache_dtype, int64_t c_stride_block, int64_t c_stride_slot,
+                                    int64_t c_stride_head, const void* k_meta, const void* v_meta,
+                                    const int32_t* block_tables, int64_t bt_stride_b,
+                                    const int32_t* context_lens, int batch, int num_q_heads,
+                                    int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                                    int max_context_len, float sm_scale, int partition_size,
+                                    hipStream_t stream) {
+  void* ws = nullptr;
+  const int st = scratch_of_current_device(&ws);
+  if (st != PKV_OK) return st;
+  // the same validation and kernels as paged_decode; the only workspace error left is a call
+  // whose partial states do not fit the static buffer
+  const int r = decode_impl(out, q, q_dtype, q_stride_b, q_stride_h, o_stride_b, o_stride_h, k_cache,
+                            v_cache, cache_dtype, c_stride_block, c_stride_slot, c_stride_head, k_meta,
+                            v_meta, block_tables, bt_stride_b, context_lens, batch, num_q_heads,
+                            num_kv_heads, head_dim, block_size, num_blocks, max_context_len, sm_scale,
+                            partition_size, ws, kScratchBytes, stream, (int64_t)block_size * num_kv_heads,
+                            num_kv_heads, 1);
+  return r == PKV_EWORKSPACE ? PKV_ESCRATCH : r;
+}

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for st in (0, -1, -2, -3, -4, 7):
+    for st in (0, -1, -2, -3, -4, -5, 7):
         assert P.pkv_status_string(st)
 
 
