@@ -62,6 +62,51 @@ __device__ __forceinline__ uint2 load_stream_u2(const void* p) {
 __device__ __forceinline__ uint32_t load_stream_u32(const void* p) {
   return __builtin_nontemporal_load(static_cast<const uint32_t*>(p));
 }
+// Buffer loads: a raw buffer resource (stride 0) over the 2^31 - 1 bytes from a wave-uniform
+// base, kept in scalar registers, plus a 32-bit per-lane byte offset and a wave-uniform byte
+// offset (soffset): no per-lane 64-bit address arithmetic.  Word 3 of the descriptor is the
+// gfx9 value for untyped dword access.  `nt` marks data read once (as load_stream_*).
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+__device__ __forceinline__ BufRsrc buf_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+template <bool NT>
+__device__ __forceinline__ uint4 buf_load_u4(BufRsrc r, uint32_t voff, uint32_t soff) {
+  typedef int i32x4_t __attribute__((ext_vector_type(4)));
+  const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, NT ? 2 : 0);
+  return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
+template <bool NT>
+__device__ __forceinline__ uint2 buf_load_u2(BufRsrc r, uint32_t voff, uint32_t soff) {
+  typedef int i32x2_t __attribute__((ext_vector_type(2)));
+  const i32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, NT ? 2 : 0);
+  return make_uint2((uint32_t)v.x, (uint32_t)v.y);
+}
+template <bool NT>
+__device__ __forceinline__ uint32_t buf_load_u32(BufRsrc r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, NT ? 2 : 0);
+}
+
+// Matrix-core product of 16 independent 4x4x4 blocks (v_mfma_f32_4x4x4{f16,bf16_1k}): block b
+// (lanes 4b .. 4b + 3) takes A[m][k] from element k of lane 4b + m, B[k][n] from element k of
+// lane 4b + n, and adds C[m][n] to register m of lane 4b + n.  The four 16-bit elements of a
+// lane's operand are the pairs (a0, a1), resp. (b0, b1), low half first.
+template <bool BF16>
+__device__ __forceinline__ f32x4_t mfma4x4x4(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1,
+                                              f32x4_t c) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t a = {a0, a1}, b = {b0, b1};
+  if constexpr (BF16) {
+    typedef short i16x4_t __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(i16x4_t, a),
+                                                  __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
+  } else {
+    typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(f16x4_t, a),
+                                              __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+  }
+}
+
 template <bool BF16>
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   if constexpr (BF16) {
@@ -143,5 +188,26 @@ __device__ __forceinline__ float group_min(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// x of lane i ^ 4 (ds_swizzle in bit-mask mode: and 0x1f, or 0, xor 4; no address register)
+__device__ __forceinline__ float swz_xor4(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x101F));
+}
+
+// Sum of the quads of a row of N lanes (16: four quads, 8: two), each lane keeping its place in
+// its quad.  For 16 lanes, rotating by 8 and then by 4 adds the same pairs in every quad,
+// (x0 + x2) + (x1 + x3) up to the order of each addition's operands, so every quad of the row
+// gets the bit-identical sum.
+template <int N>
+__device__ __forceinline__ float row_quads_sum(float x) {
+  static_assert(N == 8 || N == 16, "rows of 8 or 16 lanes");
+  if constexpr (N == 16) {
+    x += dpp_f<DPP_ROW_ROR8>(x);
+    x += dpp_f<DPP_ROW_ROR4>(x);
+  } else {
+    x += swz_xor4(x);
+  }
+  return x;
+}
 
 }  // namespace pkv

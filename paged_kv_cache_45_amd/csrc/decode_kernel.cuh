@@ -48,6 +48,10 @@
 
 namespace pkv {
 
+#ifndef PKV_PREFETCH_DEPTH
+#define PKV_PREFETCH_DEPTH 3
+#endif
+
 constexpr int kMaxWaves = 8;        // waves per workgroup at most (token streams x head group)
 constexpr int kClaimWaves = 4;      // block counters per segment (one per head wave)
 
@@ -113,6 +117,9 @@ template <int NI> struct Regs<NI, CacheKind::U3> {
 template <int G>
 struct State {
   uint32_t qv[G][4];                 // this lane's 8 query elements of each query head
+  // matrix-core score form: the lane's query elements (8 per load instruction of a chunk) of the
+  // query heads of its column (head q, and q + 4 with 8 heads), as the B operands
+  uint32_t qm[G == 8 ? 2 : 1][4][4];
   float qsum[G];                     // u3: sum of the query row (dequant hoisting)
   float m[G], l[G], zc[G];
   // own-head form (see own_head_form): this lane's query head's running max, sum, zero-point
@@ -149,6 +156,33 @@ constexpr int kMfmaMaxG = 4;
 template <int D, int G> constexpr bool own_head_form() { return G == 2 || G == 4 || G == 8; }
 // heads a lane owns: q mod G (G <= 4), or q and q + 4 (G = 8)
 template <int G> constexpr int own_heads() { return G == 8 ? 2 : 1; }
+
+// Matrix-core score form (own-head groups whose wave instruction holds one token of HPI heads,
+// i.e. HPI = 64 / (D / 8)).  The score products of a chunk's 4 tokens are 4x4x4 matrix-core
+// blocks: each quad of lanes is a block whose A operand is K (row m = token m of the chunk, the
+// lane's 4 head-dim elements of it) and whose B operand is q (column n = query head n, the same
+// 4 elements), so register m of lane n of the quad gains the partial score of token m for
+// query head n - the own-head layout (lane q holds head q) with the chunk's tokens in its
+// registers.  To feed it, the K loads are token-transposed: lane n of every quad reads token n,
+// and the chunk's 4 load instructions walk 4 slices of the head dim (lane of quad cq of a row,
+// instruction i: elements 8 j .. 8 j + 7 with j = i * (LPR / 4) + cq).  The quads of a row hold
+// partial sums over disjoint slices and are summed once per chunk.  V keeps the row-major
+// mapping (instruction i = token i).  With 8 query heads per kv head a second block set takes
+// heads 4 .. 7; with 2, columns 2 and 3 repeat heads 0 and 1.  This replaces the 4 G dot2 products
+// and the quad reduce-scatter of every token row with 2 own_heads matrix-core instructions per
+// load instruction and one row sum per chunk.
+template <int D, int G, int HPI>
+constexpr bool mq_form() { return own_head_form<D, G>() && Geo<D, HPI, G>::TPI == 1; }
+
+// Chunks whose loads are in flight at once per wave in the static-split loop (register buffers,
+// one being computed).  The 16-bit caches move 8 KB per wave per chunk and saturate the memory
+// path with two buffers (a third measured 1.5 % slower); the byte-code and 3-bit caches move
+// 2.1 KB and 1.7 KB, and with two buffers are bound by load latency, not bandwidth.
+template <int D, int G, CacheKind KIND, int HPI>
+constexpr int prefetch_depth() {
+  if constexpr (KIND == CacheKind::Same || !mq_form<D, G, HPI>() || G == 8) return 2;
+  else return PKV_PREFETCH_DEPTH;
+}
 
 // The full scores of the lane's own heads from its partial dot products d[g], for rows of LPR
 // lanes (16: D = 128; 8: D = 64).
@@ -205,6 +239,16 @@ __device__ __forceinline__ void quad_gather(const float* x, float (&out)[G]) {
   }
 }
 
+// x of lane i of the lane's quad (i known once the loops are unrolled)
+__device__ __forceinline__ uint32_t quad_lane(uint32_t x, int i) {
+  switch (i) {
+    case 0: return dpp_u<dpp_quad_bcast<0>()>(x);
+    case 1: return dpp_u<dpp_quad_bcast<1>()>(x);
+    case 2: return dpp_u<dpp_quad_bcast<2>()>(x);
+    default: return dpp_u<dpp_quad_bcast<3>()>(x);
+  }
+}
+
 template <int G, typename St>
 __device__ __forceinline__ void pv_accumulate(St& S, const float (&p)[G], float w, const float (&v)[8]) {
   if constexpr (G <= kMfmaMaxG) {
@@ -255,6 +299,12 @@ struct LaneOffsets {
   static constexpr int NI = Geo<D, HPI, G>::NI;
   uint32_t row[NI];                  // bytes from the chunk's uniform row base
   uint32_t meta[NI];                 // u3: bytes from the chunk's uniform meta base
+  // matrix-core score form: the K rows of load instruction i (token-transposed; 3-bit: the word
+  // holding the start of the lane's octet, the next word or the same one again, and the byte
+  // permute that lines the octet up); V and meta of token 0 (token i adds i slot strides)
+  uint32_t krow[NI], krow_hi[NI], ksel[NI];
+  uint32_t vrow, vrow_hi;
+  uint32_t mrow;                     // meta of token (lane mod 4) of the chunk, the lane's head
 };
 
 template <int D, int HPI, CacheKind KIND, int G>
@@ -270,16 +320,82 @@ __device__ __forceinline__ LaneOffsets<D, HPI, KIND, G> lane_offsets(const Decod
     o.row[i] = (uint32_t)((slot * p.c_ss + (int64_t)hh * p.c_sh + col) * esz);
     o.meta[i] = (uint32_t)((slot * p.m_ss + (int64_t)hh * p.m_sh) * 4);
   }
+  if constexpr (mq_form<D, G, HPI>()) {
+    const int n = c & 3, cq = c >> 2;
+    const int64_t krow0 = (int64_t)n * p.c_ss + (int64_t)hh * p.c_sh;
+#pragma unroll
+    for (int i = 0; i < Gm::NI; ++i) {
+      const int j = i * (Gm::LPR / 4) + cq;            // the lane's 8-element slice of the head dim
+      if constexpr (KIND == CacheKind::U3) {
+        // octet j = stream bits [24 j, 24 j + 24): starts at byte 3 j, in word 3 j / 4, and
+        // spills into the next word for j mod 4 in {1, 2}
+        const bool two = ((j & 3) == 1) || ((j & 3) == 2);
+        o.krow[i] = (uint32_t)((krow0 + ((3 * j) >> 2)) * 4);
+        o.krow_hi[i] = o.krow[i] + (two ? 4u : 0u);
+        o.ksel[i] = (uint32_t)((3 * j) & 3) * 0x01010101u + 0x02010100u;
+      } else {
+        o.krow[i] = (uint32_t)((krow0 + 8 * j) * esz);
+        o.krow_hi[i] = 0;
+        o.ksel[i] = 0;
+      }
+    }
+    const bool vtwo = ((c & 3) == 1) || ((c & 3) == 2);
+    o.vrow = (uint32_t)(((int64_t)hh * p.c_sh + col) * esz);
+    o.vrow_hi = o.vrow + ((KIND == CacheKind::U3 && vtwo) ? 4u : 0u);
+    o.mrow = (uint32_t)(((int64_t)n * p.m_ss + (int64_t)hh * p.m_sh) * 4);   // token n's meta
+  }
   return o;
 }
 
 // Issue the loads of one chunk: `kb`/`vb` point at the row of (block, first slot, first head
 // of the group) and `kmb`/`vmb` at its meta entry (u3), all wave-uniform.
 template <int D, int HPI, CacheKind KIND, int G>
-__device__ __forceinline__ void load_chunk(const char* kb, const char* vb, const char* kmb,
-                                           const char* vmb, const LaneOffsets<D, HPI, KIND, G>& o, int c,
+__device__ __forceinline__ void load_chunk(const DecodeParams& p, const char* kb, const char* vb,
+                                           const char* kmb, const char* vmb,
+                                           const LaneOffsets<D, HPI, KIND, G>& o, int c,
                                            Regs<Geo<D, HPI, G>::NI, KIND>& R) {
   using Gm = Geo<D, HPI, G>;
+  if constexpr (mq_form<D, G, HPI>()) {
+    // buffer loads: K token-transposed (instruction i = a head-dim slice of the chunk's 4
+    // tokens), V and meta row-major (instruction i = token i, i slot strides further on).  The K
+    // loads carry no non-temporal hint: each K instruction reads part of 16 cache lines that the
+    // chunk's other 3 K instructions read too, so the lines must stay in the vector cache until
+    // then (with the hint: fp8 decode 74.6 -> 83.1 us, 3-bit decode 131.5 -> 144.2 us on one box).
+    // V, read in whole lines by each instruction, keeps it.
+    constexpr int esz = KIND == CacheKind::U3 ? 4 : byte_kind(KIND) ? 1 : 2;
+    const uint32_t ss = (uint32_t)(p.c_ss * esz);
+    const BufRsrc kr = buf_rsrc(kb), vr = buf_rsrc(vb);
+    if constexpr (KIND == CacheKind::Same) {
+#pragma unroll
+      for (int i = 0; i < Gm::NI; ++i) {
+        R.k[i] = buf_load_u4<false>(kr, o.krow[i], 0);
+        R.v[i] = buf_load_u4<true>(vr, o.vrow, i * ss);
+      }
+    } else if constexpr (byte_kind(KIND)) {
+      // the chunk's 4 row scales of the lane's head in one load each for K and V: lane q of a
+      // quad reads token q's (slot 0 of the registers; spread over the quad when computed)
+      const BufRsrc kmr = buf_rsrc(kmb), vmr = buf_rsrc(vmb);
+      R.ks[0] = __uint_as_float(buf_load_u32<false>(kmr, o.mrow, 0));
+      R.vs[0] = __uint_as_float(buf_load_u32<false>(vmr, o.mrow, 0));
+#pragma unroll
+      for (int i = 0; i < Gm::NI; ++i) {
+        R.k[i] = buf_load_u2<false>(kr, o.krow[i], 0);
+        R.v[i] = buf_load_u2<true>(vr, o.vrow, i * ss);
+      }
+    } else {
+      const BufRsrc kmr = buf_rsrc(kmb), vmr = buf_rsrc(vmb);
+      R.km[0] = buf_load_u32<true>(kmr, o.mrow, 0);          // (s, z) of token lane mod 4
+      R.vm[0] = buf_load_u32<true>(vmr, o.mrow, 0);
+#pragma unroll
+      for (int i = 0; i < Gm::NI; ++i) {
+        R.klo[i] = buf_load_u32<false>(kr, o.krow[i], 0);
+        R.khi[i] = buf_load_u32<false>(kr, o.krow_hi[i], 0);
+        R.vlo[i] = buf_load_u32<true>(vr, o.vrow, i * ss);
+        R.vhi[i] = buf_load_u32<true>(vr, o.vrow_hi, i * ss);
+      }
+    }
+    return;
+  }
   if constexpr (KIND == CacheKind::Same) {
 #pragma unroll
     for (int i = 0; i < Gm::NI; ++i) {
@@ -326,7 +442,84 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
   float sc[NI][G];                   // every head's scores (OWN: unused)
   constexpr int HO = own_heads<G>();
   float sco[NI][HO];                 // OWN: this lane's heads' scores
-  if constexpr (KIND == CacheKind::Same || byte_kind(KIND)) {
+  // the row meta of token i (byte codes: fp32 scales; 3-bit: fp16 (s, z)): in register i of the
+  // row-major form; in the matrix-core score form lane q of each quad loaded token q's
+  [[maybe_unused]] uint32_t kmt[NI], vmt[NI];
+  if constexpr (byte_kind(KIND) || KIND == CacheKind::U3) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if constexpr (byte_kind(KIND)) {
+        kmt[i] = mq_form<D, G, HPI>() ? quad_lane(__float_as_uint(R.ks[0]), i) : __float_as_uint(R.ks[i]);
+        vmt[i] = mq_form<D, G, HPI>() ? quad_lane(__float_as_uint(R.vs[0]), i) : __float_as_uint(R.vs[i]);
+      } else {
+        kmt[i] = mq_form<D, G, HPI>() ? quad_lane(R.km[0], i) : R.km[i];
+        vmt[i] = mq_form<D, G, HPI>() ? quad_lane(R.vm[0], i) : R.vm[i];
+      }
+    }
+  }
+  if constexpr (mq_form<D, G, HPI>()) {
+    // matrix-core score form: sacc[h] register i = token i's score for the lane's column head
+    f32x4_t sacc[HO];
+#pragma unroll
+    for (int h = 0; h < HO; ++h) sacc[h] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      // the lane's 8 K elements of slice i as four packed 16-bit pairs, in the element order of
+      // the query pairs S.qm[.][i]
+      uint32_t kw[4];
+      if constexpr (KIND == CacheKind::Same) {
+        kw[0] = R.k[i].x; kw[1] = R.k[i].y; kw[2] = R.k[i].z; kw[3] = R.k[i].w;
+      } else if constexpr (byte_kind(KIND)) {
+        kw[0] = codes2_to_16<KIND, BF16, false>(R.k[i].x);
+        kw[1] = codes2_to_16<KIND, BF16, true>(R.k[i].x);
+        kw[2] = codes2_to_16<KIND, BF16, false>(R.k[i].y);
+        kw[3] = codes2_to_16<KIND, BF16, true>(R.k[i].y);
+      } else {
+        // octet j of the row starts at byte (3 j) mod 4 of (klo, khi): the permute and the
+        // packed shifts of the row-major form, pairs (code e, code e + 4)
+        const int j = i * (LPR / 4) + (c >> 2);
+        const uint32_t y = __builtin_amdgcn_perm(R.khi[i], R.klo[i],
+                                                 (uint32_t)((3 * j) & 3) * 0x01010101u + 0x02010100u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const u16x2_t sh2 = {(uint16_t)(3 * e), (uint16_t)(3 * e + 4)};
+          const uint32_t pr = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2_t, y) >> sh2) & 0x00070007u;
+          // bf16: 128 + code (exact; the 128 is folded into the zero point); fp16: the code alone
+          // is the subnormal code * 2^-24, which the matrix cores multiply exactly (the 2^24 is
+          // folded into the scale and the query sum)
+          kw[e] = BF16 ? (pr | 0x43004300u) : pr;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < HO; ++h) {
+        sacc[h] = mfma4x4x4<BF16>(kw[0], kw[1], S.qm[h][i][0], S.qm[h][i][1], sacc[h]);
+        sacc[h] = mfma4x4x4<BF16>(kw[2], kw[3], S.qm[h][i][2], S.qm[h][i][3], sacc[h]);
+      }
+    }
+    // the row's quads summed over their head-dim slices, bit-identically in every quad
+#pragma unroll
+    for (int h = 0; h < HO; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sacc[h][r] = row_quads_sum<LPR>(sacc[h][r]);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if constexpr (KIND == CacheKind::U3) {
+        // q.(code - z)*s = s * (q.code - z * sum(q)); bf16 codes carry +128 (folded into z);
+        // fp16: sacc is q.code * 2^-24 and S.qso the query sum * 2^-24
+        const float ks = f16_lo(kmt[i]), kz = f16_hi(kmt[i]);
+        const float off = BF16 ? 128.f + kz : kz;
+        const float kscl = BF16 ? p.scale_log2 : p.scale_log2 * 0x1p24f;
+#pragma unroll
+        for (int h = 0; h < HO; ++h)
+          sco[i][h] = valid[i] ? ks * (sacc[h][i] - off * S.qso[h]) * kscl : neg_inf();
+      } else {
+        float scl = p.scale_log2;
+        if constexpr (byte_kind(KIND)) scl *= __uint_as_float(kmt[i]);
+#pragma unroll
+        for (int h = 0; h < HO; ++h) sco[i][h] = valid[i] ? sacc[h][i] * scl : neg_inf();
+      }
+    }
+  } else if constexpr (KIND == CacheKind::Same || byte_kind(KIND)) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       uint32_t kw[4];
@@ -348,7 +541,7 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
         for (int e = 0; e < 4; ++e) d[g] = dot2<BF16>(S.qv[g][e], kw[e], d[g]);
       }
       float scl = p.scale_log2;
-      if constexpr (byte_kind(KIND)) scl *= R.ks[i];
+      if constexpr (byte_kind(KIND)) scl *= __uint_as_float(kmt[i]);
       if constexpr (OWN) {
         float so[HO];
         reduce_own<G, LPR>(d, q, so);
@@ -392,7 +585,7 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
 #pragma unroll
         for (int e = 0; e < 4; ++e) d[g] = dot2<BF16>(S.qv[g][e], cp[e], d[g]);
       }
-      const float ks = f16_lo(R.km[i]), kz = f16_hi(R.km[i]);
+      const float ks = f16_lo(kmt[i]), kz = f16_hi(kmt[i]);
       const float off = BF16 ? 128.f + kz : kz;
       if constexpr (OWN) {
         float so[HO];
@@ -424,15 +617,16 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
   float mxo[HO];
   bool grow = false;
   if constexpr (OWN) {
+    // every head is owned by a lane of every quad, whose own maximum equals the replicated one,
+    // so comparing the own heads decides for the wave; the replicated maxima of every head are
+    // gathered only when some grew
 #pragma unroll
     for (int h = 0; h < HO; ++h) {
       mxo[h] = sco[0][h];
 #pragma unroll
       for (int i = 1; i < NI; ++i) mxo[h] = fmaxf(mxo[h], sco[i][h]);
+      grow |= mxo[h] > S.mo[h];
     }
-    quad_gather<G>(mxo, mx);
-#pragma unroll
-    for (int g = 0; g < G; ++g) grow |= mx[g] > S.m[g];
   } else {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -443,6 +637,7 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
     }
   }
   if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    if constexpr (OWN) quad_gather<G>(mxo, mx);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float mn = fmaxf(S.m[g], mx[g]);
@@ -504,7 +699,7 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
       else pv_accumulate<G>(S, pp[i], 1.f, vf);
     } else if constexpr (byte_kind(KIND)) {
       uint32_t vw0 = R.v[i].x, vw1 = R.v[i].y;
-      float vs = R.vs[i];
+      float vs = __uint_as_float(vmt[i]);
       if (MASKED && !valid[i]) { vw0 = vw1 = 0u; vs = 0.f; }          // poisoned tails stay out
       codes2_to_f32<KIND, false>(vw0, vf[0], vf[1]);
       codes2_to_f32<KIND, true>(vw0, vf[2], vf[3]);
@@ -518,8 +713,8 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
       const uint32_t y = __builtin_amdgcn_perm(R.vhi[i], R.vlo[i], (uint32_t)((3 * c) & 3) * 0x01010101u + 0x02010100u);
 #pragma unroll
       for (int e = 0; e < 8; ++e) vf[e] = (float)((y >> (e < 5 ? 3 * e : 3 * e + 8)) & 7u);
-      const float vs = valid[i] ? f16_lo(R.vm[i]) : 0.f;
-      const float vz = valid[i] ? f16_hi(R.vm[i]) : 0.f;
+      const float vs = valid[i] ? f16_lo(vmt[i]) : 0.f;
+      const float vz = valid[i] ? f16_hi(vmt[i]) : 0.f;
       // sum_t p (code - z) s = sum_t (p s) code - sum_t (p s) z
       if constexpr (OWN) {
 #pragma unroll
@@ -584,30 +779,46 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, State<G>& S, in
     const int64_t slot0 = tok0 & (p.block_size - 1);
     const int64_t rowb = (phys * p.c_sb + slot0 * p.c_ss) * esz;
     const int64_t metab = (phys * p.m_sb + slot0 * p.m_ss) * 4;
-    load_chunk<D, HPI, KIND, G>(kc + rowb, vc + rowb, kmc + metab, vmc + metab, lo, c, regs);
+    load_chunk<D, HPI, KIND, G>(p, kc + rowb, vc + rowb, kmc + metab, vmc + metab, lo, c, regs);
   };
   auto tok_of = [&](int k) { return t0 + k * Gm::CT + tr; };
-  int k = claim();
-  if (k < n_plain) {
-    R ra, rb;
-    issue(k, ra);
-    for (;;) {
-      const int k1 = claim();
-      if (k1 < n_plain) issue(k1, rb);
-      compute_chunk<D, G, BF16, KIND, HPI, false>(p, S, ra, tok_of(k), t1, c);
-      k = k1;
-      if (k >= n_plain) break;
-      const int k2 = claim();
-      if (k2 < n_plain) issue(k2, ra);
-      compute_chunk<D, G, BF16, KIND, HPI, false>(p, S, rb, tok_of(k), t1, c);
-      k = k2;
-      if (k >= n_plain) break;
+  // A ring of NB register buffers: the loads of the next NB - 1 claimed chunks are in flight
+  // while one chunk is computed.  Claims only grow, so the first claim at or past n_plain (this
+  // wave's k_end) ends the claiming; exactly one wave gets n_plain itself, and it takes the
+  // ragged last chunk.
+  constexpr int NB = prefetch_depth<D, G, KIND, HPI>();
+  int k_end = -1;
+  auto next = [&]() {
+    if (k_end >= 0) return k_end;
+    const int k = claim();
+    if (k >= n_plain) k_end = k;
+    return k;
+  };
+  R r[NB];
+  int kq[NB];
+#pragma unroll
+  for (int b = 0; b < NB - 1; ++b) {
+    kq[b] = next();
+    if (kq[b] < n_plain) issue(kq[b], r[b]);
+  }
+  bool done = kq[0] >= n_plain;
+  while (!done) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int nb = (b + NB - 1) % NB;           // the buffer computed last, free again
+      kq[nb] = next();
+      if (kq[nb] < n_plain) issue(kq[nb], r[nb]);
+      compute_chunk<D, G, BF16, KIND, HPI, false>(p, S, r[b], tok_of(kq[b]), t1, c);
+      if (kq[(b + 1) % NB] >= n_plain) {
+        done = true;
+        break;
+      }
     }
   }
-  if (ragged && k == n_plain) {          // the ragged last chunk, taken by exactly one wave
+  if (ragged && k_end == n_plain) {      // the ragged last chunk, taken by exactly one wave
     R regs;
-    issue(k, regs);
-    compute_chunk<D, G, BF16, KIND, HPI, true>(p, S, regs, tok_of(k), t1, c);
+    issue(n_plain, regs);
+    compute_chunk<D, G, BF16, KIND, HPI, true>(p, S, regs, tok_of(n_plain), t1, c);
   }
 }
 
@@ -661,7 +872,7 @@ __device__ __forceinline__ void run_claimed(const DecodeParams& p, State<G>& S, 
     const int64_t slot0 = l.slot + k * Gm::CT;
     const int64_t rowb = (l.phys * p.c_sb + slot0 * p.c_ss) * esz;
     const int64_t metab = (l.phys * p.m_sb + slot0 * p.m_ss) * 4;
-    load_chunk<D, HPI, KIND, G>(kc + rowb, vc + rowb, kmc + metab, vmc + metab, lo, c, regs);
+    load_chunk<D, HPI, KIND, G>(p, kc + rowb, vc + rowb, kmc + metab, vmc + metab, lo, c, regs);
   };
   int uc = take(__builtin_amdgcn_readfirstlane(claim_async()));
   int un = take(__builtin_amdgcn_readfirstlane(claim_async()));
@@ -820,10 +1031,18 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
     const int h = hg * p.heads_per_group + hh;             // kv head of this lane's row
 
     State<G> S;
+    constexpr bool MQ = mq_form<D, G, HPI>();
+    const uint16_t* q_row = static_cast<const uint16_t*>(p.q) + b * p.q_sb + (int64_t)h * G * p.q_sh;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.q) +
-                                                      b * p.q_sb + (int64_t)(h * G + g) * p.q_sh + c * 8);
+      S.qsum[g] = 0.f;
+      S.m[g] = neg_inf();
+      S.l[g] = 0.f;
+      S.zc[g] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) PKV_ACC(S, g, e) = 0.f;
+      if constexpr (MQ) continue;
+      const uint4 v = *reinterpret_cast<const uint4*>(q_row + (int64_t)g * p.q_sh + c * 8);
       if constexpr (KIND == CacheKind::U3) {
         // pairs (q[e], q[e + 4]) of the lane's 8 elements, the order the 3-bit codes unpack in
         S.qv[g][0] = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
@@ -833,18 +1052,12 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
       } else {
         S.qv[g][0] = v.x; S.qv[g][1] = v.y; S.qv[g][2] = v.z; S.qv[g][3] = v.w;
       }
-      S.qsum[g] = 0.f;
       if constexpr (KIND == CacheKind::U3) {
         float s = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) s += h_lo<BF16>(S.qv[g][e]) + h_hi<BF16>(S.qv[g][e]);
         S.qsum[g] = group_sum<Gm::LPR>(s);
       }
-      S.m[g] = neg_inf();
-      S.l[g] = 0.f;
-      S.zc[g] = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) PKV_ACC(S, g, e) = 0.f;
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -857,6 +1070,34 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
 #pragma unroll
       for (int g = 1; g < G; ++g)
         if (own == g) S.qso[h] = S.qsum[g];
+    }
+    if constexpr (MQ) {
+      // B operands of the score products: the lane's column head (lane mod 4, with 8 heads also
+      // + 4) at the head-dim slice j of each load instruction i; 3-bit: pairs (q[e], q[e + 4]),
+      // the order its codes unpack in, and the head's query sum for the zero point
+#pragma unroll
+      for (int hs = 0; hs < own_heads<G>(); ++hs) {
+        const int g = (G == 8) ? (lane & 3) + 4 * hs : (lane & 3 & (G - 1));
+        float qs = 0.f;
+#pragma unroll
+        for (int i = 0; i < Gm::NI; ++i) {
+          const int j = i * (Gm::LPR / 4) + (c >> 2);
+          const uint4 v = *reinterpret_cast<const uint4*>(q_row + (int64_t)g * p.q_sh + j * 8);
+          if constexpr (KIND == CacheKind::U3) {
+            S.qm[hs][i][0] = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
+            S.qm[hs][i][1] = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
+            S.qm[hs][i][2] = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
+            S.qm[hs][i][3] = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qs += h_lo<BF16>(S.qm[hs][i][e]) + h_hi<BF16>(S.qm[hs][i][e]);
+          } else {
+            S.qm[hs][i][0] = v.x; S.qm[hs][i][1] = v.y; S.qm[hs][i][2] = v.z; S.qm[hs][i][3] = v.w;
+          }
+        }
+        // fp16 scores are taken with the 3-bit codes as code * 2^-24 (exactly): the query sum
+        // is kept in the same units
+        if constexpr (KIND == CacheKind::U3) S.qso[hs] = row_quads_sum<Gm::LPR>(qs) * (BF16 ? 1.f : 0x1p-24f);
+      }
     }
     if (seg_i > 0 && threadIdx.x < kMaxWaves) s_cnt[(seg_i + 1) & 1][threadIdx.x] = 0;
     int* cnt = &s_cnt[seg_i & 1][wv];
