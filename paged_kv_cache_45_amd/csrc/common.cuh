@@ -66,9 +66,12 @@ __device__ __forceinline__ uint32_t load_stream_u32(const void* p) {
 // base, kept in scalar registers, plus a 32-bit per-lane byte offset and a wave-uniform byte
 // offset (soffset): no per-lane 64-bit address arithmetic.  Word 3 of the descriptor is the
 // gfx9 value for untyped dword access.  `nt` marks data read once (as load_stream_*).
+// A resource of 0 records makes every load through it return zeros without a memory access:
+// loads that must be issued on every path (so that the wait counts stay exact) but whose data
+// is not needed use one.
 typedef __amdgpu_buffer_rsrc_t BufRsrc;
-__device__ __forceinline__ BufRsrc buf_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+__device__ __forceinline__ BufRsrc buf_rsrc(const void* base, int num_records = 0x7fffffff) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num_records, 0x00020000);
 }
 template <bool NT>
 __device__ __forceinline__ uint4 buf_load_u4(BufRsrc r, uint32_t voff, uint32_t soff) {

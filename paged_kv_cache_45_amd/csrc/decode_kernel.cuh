@@ -353,9 +353,12 @@ template <int D, int HPI, CacheKind KIND, int G>
 __device__ __forceinline__ void load_chunk(const DecodeParams& p, const char* kb, const char* vb,
                                            const char* kmb, const char* vmb,
                                            const LaneOffsets<D, HPI, KIND, G>& o, int c,
-                                           Regs<Geo<D, HPI, G>::NI, KIND>& R) {
+                                           Regs<Geo<D, HPI, G>::NI, KIND>& R, bool live = true) {
   using Gm = Geo<D, HPI, G>;
   if constexpr (mq_form<D, G, HPI>()) {
+    // a chunk that is not live (past the end of the range) is loaded through resources of 0
+    // records: zeros, no memory access, the same instructions
+    const int nrec = live ? 0x7fffffff : 0;
     // buffer loads: K token-transposed (instruction i = a head-dim slice of the chunk's 4
     // tokens), V and meta row-major (instruction i = token i, i slot strides further on).  The K
     // loads carry no non-temporal hint: each K instruction reads part of 16 cache lines that the
@@ -364,7 +367,7 @@ __device__ __forceinline__ void load_chunk(const DecodeParams& p, const char* kb
     // V, read in whole lines by each instruction, keeps it.
     constexpr int esz = KIND == CacheKind::U3 ? 4 : byte_kind(KIND) ? 1 : 2;
     const uint32_t ss = (uint32_t)(p.c_ss * esz);
-    const BufRsrc kr = buf_rsrc(kb), vr = buf_rsrc(vb);
+    const BufRsrc kr = buf_rsrc(kb, nrec), vr = buf_rsrc(vb, nrec);
     if constexpr (KIND == CacheKind::Same) {
 #pragma unroll
       for (int i = 0; i < Gm::NI; ++i) {
@@ -374,7 +377,7 @@ __device__ __forceinline__ void load_chunk(const DecodeParams& p, const char* kb
     } else if constexpr (byte_kind(KIND)) {
       // the chunk's 4 row scales of the lane's head in one load each for K and V: lane q of a
       // quad reads token q's (slot 0 of the registers; spread over the quad when computed)
-      const BufRsrc kmr = buf_rsrc(kmb), vmr = buf_rsrc(vmb);
+      const BufRsrc kmr = buf_rsrc(kmb, nrec), vmr = buf_rsrc(vmb, nrec);
       R.ks[0] = __uint_as_float(buf_load_u32<false>(kmr, o.mrow, 0));
       R.vs[0] = __uint_as_float(buf_load_u32<false>(vmr, o.mrow, 0));
 #pragma unroll
@@ -383,7 +386,7 @@ __device__ __forceinline__ void load_chunk(const DecodeParams& p, const char* kb
         R.v[i] = buf_load_u2<true>(vr, o.vrow, i * ss);
       }
     } else {
-      const BufRsrc kmr = buf_rsrc(kmb), vmr = buf_rsrc(vmb);
+      const BufRsrc kmr = buf_rsrc(kmb, nrec), vmr = buf_rsrc(vmb, nrec);
       R.km[0] = buf_load_u32<true>(kmr, o.mrow, 0);          // (s, z) of token lane mod 4
       R.vm[0] = buf_load_u32<true>(vmr, o.mrow, 0);
 #pragma unroll
@@ -755,59 +758,77 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, State<G>& S, in
   const char* vmc = static_cast<const char*>(p.v_meta) + (int64_t)h_first * p.m_sh * 4;
   typedef __attribute__((address_space(3))) int LdsInt;
   LdsInt* const cnt_lds = (LdsInt*)cnt;                   // an LDS atomic (ds_add_rtn, lgkmcnt)
-  auto claim = [&]() {
-    int v = 0;
-    if (lane == 0) v = __hip_atomic_fetch_add(cnt_lds, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    return __builtin_amdgcn_readfirstlane(v);
-  };
   // physical block ids of chunks [win, win + 64), lane k <-> chunk win + k; claims only grow,
   // so the window only moves forward
   int win = 0, bt_lane = 0;
   bool have = false;
-  auto issue = [&](int k, R& regs) {
-    if (!have || k - win >= 64) {
-      win = k;
-      have = true;
-      bt_lane = 0;
-      if (win + lane < nk) {
-        const int e = bt_row[(t0 + (win + lane) * Gm::CT) >> p.log2_bs];
-        bt_lane = (int)min<int64_t>(max(e, 0), p.num_blocks - 1);   // out-of-range ids clamped
+  // Loads of chunk k (live: k is a chunk of the range).  In the matrix-core form a chunk that is
+  // not live is issued too, through resources of 0 records: every path through the loop then
+  // issues the same loads, so the compiler's wait counts for the chunks in flight stay exact
+  // (a load issued on one path only makes it wait for every load at the join, the ones just
+  // issued included).  The row-major form skips it.
+  auto issue = [&](int k, R& regs, bool live) {
+    int64_t phys = 0;
+    if (live) {
+      if (!have || k - win >= 64) {
+        win = k;
+        have = true;
+        bt_lane = 0;
+        if (win + lane < nk) {
+          const int e = bt_row[(t0 + (win + lane) * Gm::CT) >> p.log2_bs];
+          bt_lane = (int)min<int64_t>(max(e, 0), p.num_blocks - 1);   // out-of-range ids clamped
+        }
       }
+      phys = __builtin_amdgcn_readlane(bt_lane, k - win);
+    } else if constexpr (!mq_form<D, G, HPI>()) {
+      return;
     }
     const int tok0 = t0 + k * Gm::CT;
-    const int64_t phys = __builtin_amdgcn_readlane(bt_lane, k - win);
     const int64_t slot0 = tok0 & (p.block_size - 1);
     const int64_t rowb = (phys * p.c_sb + slot0 * p.c_ss) * esz;
     const int64_t metab = (phys * p.m_sb + slot0 * p.m_ss) * 4;
-    load_chunk<D, HPI, KIND, G>(p, kc + rowb, vc + rowb, kmc + metab, vmc + metab, lo, c, regs);
+    load_chunk<D, HPI, KIND, G>(p, kc + rowb, vc + rowb, kmc + metab, vmc + metab, lo, c, regs, live);
   };
   auto tok_of = [&](int k) { return t0 + k * Gm::CT + tr; };
   // A ring of NB register buffers: the loads of the next NB - 1 claimed chunks are in flight
-  // while one chunk is computed.  Claims only grow, so the first claim at or past n_plain (this
-  // wave's k_end) ends the claiming; exactly one wave gets n_plain itself, and it takes the
-  // ragged last chunk.
+  // while one chunk is computed.  Each claim (an LDS atomic on the head wave's counter, by lane
+  // 0) is issued before the chunk that precedes its use is computed, so its latency is hidden.
+  // Claims only grow, so the first claim at or past n_plain (this wave's k_end) ends the
+  // claiming; exactly one wave gets n_plain itself, and it takes the ragged last chunk.
   constexpr int NB = prefetch_depth<D, G, KIND, HPI>();
   int k_end = -1;
-  auto next = [&]() {
+  auto claim_raw = [&]() {                        // the atomic in flight (lane 0's result)
+    int v = 0;
+    if (k_end < 0 && lane == 0)
+      v = __hip_atomic_fetch_add(cnt_lds, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return v;
+  };
+  auto take = [&](int raw) {                      // the claimed chunk
     if (k_end >= 0) return k_end;
-    const int k = claim();
+    const int k = __builtin_amdgcn_readfirstlane(raw);
     if (k >= n_plain) k_end = k;
     return k;
   };
   R r[NB];
   int kq[NB];
+  int raw = claim_raw();
 #pragma unroll
   for (int b = 0; b < NB - 1; ++b) {
-    kq[b] = next();
-    if (kq[b] < n_plain) issue(kq[b], r[b]);
+    kq[b] = take(raw);
+    raw = claim_raw();
+    issue(kq[b], r[b], kq[b] < n_plain);
   }
   bool done = kq[0] >= n_plain;
   while (!done) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int nb = (b + NB - 1) % NB;           // the buffer computed last, free again
-      kq[nb] = next();
-      if (kq[nb] < n_plain) issue(kq[nb], r[nb]);
+      kq[nb] = take(raw);
+      raw = claim_raw();
+      issue(kq[nb], r[nb], kq[nb] < n_plain);
+      // keep the scheduler from hoisting this chunk's first products above the new loads: they
+      // would then wait for all loads in flight before the next chunk's are even issued
+      __builtin_amdgcn_sched_barrier(0);
       compute_chunk<D, G, BF16, KIND, HPI, false>(p, S, r[b], tok_of(kq[b]), t1, c);
       if (kq[(b + 1) % NB] >= n_plain) {
         done = true;
@@ -817,7 +838,7 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, State<G>& S, in
   }
   if (ragged && k_end == n_plain) {      // the ragged last chunk, taken by exactly one wave
     R regs;
-    issue(n_plain, regs);
+    issue(n_plain, regs, true);
     compute_chunk<D, G, BF16, KIND, HPI, true>(p, S, regs, tok_of(n_plain), t1, c);
   }
 }
@@ -872,7 +893,7 @@ __device__ __forceinline__ void run_claimed(const DecodeParams& p, State<G>& S, 
     const int64_t slot0 = l.slot + k * Gm::CT;
     const int64_t rowb = (l.phys * p.c_sb + slot0 * p.c_ss) * esz;
     const int64_t metab = (l.phys * p.m_sb + slot0 * p.m_ss) * 4;
-    load_chunk<D, HPI, KIND, G>(p, kc + rowb, vc + rowb, kmc + metab, vmc + metab, lo, c, regs);
+    load_chunk<D, HPI, KIND, G>(p, kc + rowb, vc + rowb, kmc + metab, vmc + metab, lo, c, regs, true);
   };
   int uc = take(__builtin_amdgcn_readfirstlane(claim_async()));
   int un = take(__builtin_amdgcn_readfirstlane(claim_async()));
