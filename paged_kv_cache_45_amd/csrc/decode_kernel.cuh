@@ -889,26 +889,34 @@ __device__ __forceinline__ void run_claimed(const DecodeParams& p, State<G>& S, 
     }
     return l;
   };
-  auto issue = [&](const Loc& l, int k, R& regs) {         // chunk k (tokens k * CT) of a unit
+  // chunk k (tokens k * CT) of a unit; in the matrix-core form the first chunk of a unit past
+  // the end is issued too, through resources of 0 records (the same loads on every path keep the
+  // compiler's wait counts exact; see run_range)
+  auto issue = [&](const Loc& l, int k, R& regs, bool live) {
+    if constexpr (!mq_form<D, G, HPI>()) {
+      if (!live) return;
+    }
     const int64_t slot0 = l.slot + k * Gm::CT;
     const int64_t rowb = (l.phys * p.c_sb + slot0 * p.c_ss) * esz;
     const int64_t metab = (l.phys * p.m_sb + slot0 * p.m_ss) * 4;
-    load_chunk<D, HPI, KIND, G>(p, kc + rowb, vc + rowb, kmc + metab, vmc + metab, lo, c, regs, true);
+    load_chunk<D, HPI, KIND, G>(p, kc + rowb, vc + rowb, kmc + metab, vmc + metab, lo, c, regs, live);
   };
   int uc = take(__builtin_amdgcn_readfirstlane(claim_async()));
   int un = take(__builtin_amdgcn_readfirstlane(claim_async()));
   Loc pc = loc_of(uc);
   R ra, rb;
-  if (uc < nu) issue(pc, 0, ra);
+  issue(pc, 0, ra, uc < nu);
   while (uc < nu) {
     const int pending = (un < nu) ? claim_async() : 0;    // the claim after next
     const Loc pn = loc_of(un);
     const int tok = (uc << p.log2_claim) + tr;
     for (int k = 0; k < my_n; k += 2) {
-      issue(pc, k + 1, rb);
+      issue(pc, k + 1, rb, true);
+      __builtin_amdgcn_sched_barrier(0);
       compute_chunk<D, G, BF16, KIND, HPI, false>(p, S, ra, tok + k * Gm::CT, 0, c);
-      if (k + 2 < my_n) issue(pc, k + 2, ra);
-      else if (un < nu) issue(pn, 0, ra);
+      if (k + 2 < my_n) issue(pc, k + 2, ra, true);
+      else issue(pn, 0, ra, un < nu);
+      __builtin_amdgcn_sched_barrier(0);
       compute_chunk<D, G, BF16, KIND, HPI, false>(p, S, rb, tok + (k + 1) * Gm::CT, 0, c);
     }
     uc = un;

@@ -212,3 +212,17 @@ def test_contiguous_cache_through_the_paged_oracle():
     got = paged_decode_ref(q, PoolView("same", pk, dtype="f16"), PoolView("same", pv, dtype="f16"), bt,
                            np.array(lens), BS, H, 0.3)
     assert np.allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_to_f32_matches_torch_on_every_16bit_pattern():
+    """The oracle's widening of fp16 and bf16 bit patterns against torch's own conversions, on
+    all 65,536 patterns of each (NaN patterns compared as NaN)."""
+    import torch
+    from oracle.append import to_f32
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    for name, dt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
+        got = to_f32(bits, name)
+        want = torch.from_numpy(bits.view(np.int16)).view(dt).to(torch.float32).numpy()
+        nan = np.isnan(want)
+        assert np.array_equal(np.isnan(got), nan), name
+        assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32)), name

@@ -74,9 +74,24 @@ def _case(seed, lens, Hq, Hkv, D, BS, spare=3):
     return q, K, V, kp, vp, bt, np.array(lens, dtype=np.int32)
 
 
-def _ref(q, kp, vp, bt, lens, BS, Hkv, sm, **kw):
-    return paged_decode_ref(q, PoolView("same", kp, dtype="f16"), PoolView("same", vp, dtype="f16"),
+def _ref(q, kp, vp, bt, lens, BS, Hkv, sm, dtype="f16", **kw):
+    return paged_decode_ref(q, PoolView("same", kp, dtype=dtype), PoolView("same", vp, dtype=dtype),
                             bt, lens, BS, Hkv, sm, **kw)
+
+
+def _bf16_case(seed, lens, Hq, Hkv, D, BS, spare=3):
+    """The bf16 form of _case: values rounded to bf16 by torch's own cast (not the oracle's
+    widening), bit patterns from torch, the dense side in float64 from the same bf16 values."""
+    rng = np.random.default_rng(seed)
+    gen = lambda shape: torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(torch.bfloat16)
+    K = [gen((L, Hkv, D)) for L in lens]
+    V = [gen((L, Hkv, D)) for L in lens]
+    q = gen((len(lens), Hq, D))
+    nb = sum(-(-L // BS) for L in lens) + spare
+    kp, vp, bt = _scatter_dense(rng, [_bits(k) for k in K], [_bits(v) for v in V], BS, nb, dtype="bf16")
+    f64 = lambda t: t.to(torch.float64).numpy()
+    return (f64(q), [f64(k) for k in K], [f64(v) for v in V], kp, vp, bt,
+            np.array(lens, dtype=np.int32))
 
 
 @pytest.mark.parametrize("lens,Hq,Hkv,D,BS", [
@@ -89,6 +104,22 @@ def test_brute_force_dense_sdpa(lens, Hq, Hkv, D, BS):
     q, K, V, kp, vp, bt, L = _case(3, lens, Hq, Hkv, D, BS)
     sm = 1.0 / math.sqrt(D)
     got = _ref(q, kp, vp, bt, L, BS, Hkv, sm)
+    want = _sdpa_dense(q, K, V, sm, Hq // Hkv)
+    assert np.max(np.abs(got - want)) < 1e-12
+
+
+@pytest.mark.parametrize("lens,Hq,Hkv,D,BS", [
+    ([11, 26], 4, 4, 64, 16),
+    ([1, 17, 33, 64], 8, 2, 64, 16),
+    ([513, 100], 32, 8, 128, 16),
+    ([200], 64, 8, 128, 64),
+])
+def test_brute_force_dense_sdpa_bf16(lens, Hq, Hkv, D, BS):
+    """bf16 pools (the Llama-8B and long-context dtype) against torch's float64 SDPA on the
+    same bf16 values, the pools' bit patterns written by torch's bf16 cast."""
+    q, K, V, kp, vp, bt, L = _bf16_case(5, lens, Hq, Hkv, D, BS)
+    sm = 1.0 / math.sqrt(D)
+    got = _ref(q, kp, vp, bt, L, BS, Hkv, sm, dtype="bf16")
     want = _sdpa_dense(q, K, V, sm, Hq // Hkv)
     assert np.max(np.abs(got - want)) < 1e-12
 
