@@ -32,12 +32,15 @@
 //    waves are head waves (HPI heads each) times token streams (up to 4): the token streams
 //    of a head wave share its chunks out through an LDS counter and merge their states
 //    through LDS at the end of each segment.
-//  * QK: v_dot2_f32_{bf16,f16} on packed pairs and a DPP reduction inside the lane row;
-//    each row keeps its own online-softmax state (m, l in log2 units, the lane's 8
-//    accumulator columns per query head).
-//  * Physical block ids of up to 64 chunks are fetched with one vector load (lane k <->
-//    k-th chunk) and read back with v_readlane; the next chunk's K/V loads are issued before
-//    the current chunk is computed (two register buffers).
+//  * QK: where a wave instruction holds one token of HPI heads (the matrix-core form), the
+//    scores of a chunk are v_mfma_f32_4x4x4 products with K token-transposed (a quad's lanes
+//    hold 4 tokens) and the q heads as columns, summed over the quads of a row by DPP; else
+//    v_dot2_f32_{bf16,f16} on packed pairs and a DPP reduction inside the lane row.  Each
+//    lane keeps the online-softmax state of its own query heads (m, l in log2 units, the
+//    lane's 8 accumulator columns per query head).
+//  * Physical block ids of up to 64 blocks are fetched with one vector load (lane j <->
+//    j-th block) and read back with v_readlane; the K/V loads of the next chunks are issued
+//    before the current chunk is computed (a ring of register buffers).
 #pragma once
 #include <algorithm>
 #include <type_traits>
@@ -737,7 +740,7 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
 // head wave take the chunks from a counter in LDS (`cnt`, zero at the start) rather than a
 // fixed interleave, so that a wave that streams faster (the SIMD issues the oldest waves
 // first) takes more chunks and the workgroup's waves finish the range together.  Physical
-// block ids of up to 64 chunks are fetched with one vector load (lane k <-> k-th chunk of the
+// block ids of up to 64 blocks are fetched with one vector load (lane j <-> j-th block of the
 // window) and read back with v_readlane; the next chunk's K/V loads are issued before the
 // current chunk is computed (two register buffers).
 template <int D, int G, bool BF16, CacheKind KIND, int HPI>
@@ -758,8 +761,11 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, State<G>& S, in
   const char* vmc = static_cast<const char*>(p.v_meta) + (int64_t)h_first * p.m_sh * 4;
   typedef __attribute__((address_space(3))) int LdsInt;
   LdsInt* const cnt_lds = (LdsInt*)cnt;                   // an LDS atomic (ds_add_rtn, lgkmcnt)
-  // physical block ids of chunks [win, win + 64), lane k <-> chunk win + k; claims only grow,
-  // so the window only moves forward
+  // physical block ids of the request's blocks [win, win + 64), lane j <-> block win + j: one
+  // vector load covers 64 blocks (1024 tokens or more), so a range reloads it rarely (a reload
+  // waits for every load in flight before it); claims only grow, so the window only moves
+  // forward
+  const int last_blk = (t1 - 1) >> p.log2_bs;
   int win = 0, bt_lane = 0;
   bool have = false;
   // Loads of chunk k (live: k is a chunk of the range).  In the matrix-core form a chunk that is
@@ -770,16 +776,17 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, State<G>& S, in
   auto issue = [&](int k, R& regs, bool live) {
     int64_t phys = 0;
     if (live) {
-      if (!have || k - win >= 64) {
-        win = k;
+      const int blk = (t0 + k * Gm::CT) >> p.log2_bs;
+      if (!have || blk - win >= 64) {
+        win = blk;
         have = true;
         bt_lane = 0;
-        if (win + lane < nk) {
-          const int e = bt_row[(t0 + (win + lane) * Gm::CT) >> p.log2_bs];
+        if (win + lane <= last_blk) {
+          const int e = bt_row[win + lane];
           bt_lane = (int)min<int64_t>(max(e, 0), p.num_blocks - 1);   // out-of-range ids clamped
         }
       }
-      phys = __builtin_amdgcn_readlane(bt_lane, k - win);
+      phys = __builtin_amdgcn_readlane(bt_lane, blk - win);
     } else if constexpr (!mq_form<D, G, HPI>()) {
       return;
     }
