@@ -31,6 +31,12 @@ of the remaining shapes:
   dual-stacked-decode  the Llama-8B decode shape over the dual-stacked block layout
                      [num_blocks, 2, num_kv_heads, block_size, head_dim], as strided views (KV GB/s)
   copy-calibration   a plain device copy of 1 GiB, the reference for HBM byte counters
+  add-calibration    torch's elementwise add with the mixed fp8 append's traffic (64.26 MB,
+                     two bytes read per byte written): what a plain streaming kernel reaches
+                     at that size
+
+--pad-frac sets the mixed append's share of padding slots (default 0.10), for the check
+that the bytes it fetches follow the valid tokens.
 """
 from __future__ import annotations
 
@@ -408,7 +414,7 @@ def run_mixed_append(args, P, W):
     copies in rotation so that neither the inputs nor the pool stay in the Infinity Cache."""
     import torch
     n_copies = 8
-    wl = W.mixed_append("cuda")
+    wl = W.mixed_append("cuda", pad_frac=args.pad_frac)
     T = wl.slot_mapping.numel()
     valid = int((wl.slot_mapping >= 0).sum())
     H, D, BS, NB = wl.num_kv_heads, wl.head_dim, wl.block_size, wl.num_blocks
@@ -446,6 +452,7 @@ def run_mixed_append(args, P, W):
     alg = valid * (2 * H * D * 2 + 2 * H * D + 2 * H * 4) + T * 8
     st = stats_us(ms)
     config = {"workload": "mixed-prefill-decode-append-fp8", "tokens": T, "valid_tokens": valid,
+              "pad_frac": args.pad_frac,
               "num_kv_heads": H, "head_dim": D, "block_size": BS, "input": "bf16",
               "cache": "fp8 e4m3fn + fp32 per-row scale", "copies_rotated": n_copies}
     rec = base_record(args, "append tokens/s (mixed prefill + decode, fp8 cache)",
@@ -857,6 +864,32 @@ def pack3_cpu_baseline(values, want_packed):
                       "(vectorised numpy, one thread), 1 rep"}
 
 
+def run_add_calibration(args, P, W):
+    """torch.add(a, b, out=c) over bf16 tensors whose traffic matches the mixed fp8 append's
+    algorithmic bytes (two thirds read, one third written), 8 sets in rotation: the rate a
+    plain streaming kernel reaches at that size, beside the append's."""
+    import torch
+    total = 64263976
+    n = total // 3 // 2
+    sets = [tuple(torch.randn(n, device="cuda", dtype=torch.bfloat16) for _ in range(3)) for _ in range(8)]
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        a, b, c = sets[i % 8]
+        torch.add(a, b, out=c)
+
+    for i in range(max(1, args.warmup)):
+        call(i)
+    ms = call_times_ms(call, args, stream)
+    st = stats_us(ms)
+    config = {"workload": "add-calibration", "bytes_read": 4 * n, "bytes_written": 2 * n, "sets_rotated": 8}
+    rec = base_record(args, "elementwise add GB/s (read + write)", 6 * n / (st["median"] * 1e-6) / 1e9,
+                      "GB/s", st["median"] * 1e-3, "bf16", config)
+    rec.update({"add_us": st, "timing": "event-timed eager calls",
+                "roofline": hbm_roofline("torch add", 6 * n, ms)})
+    return rec
+
+
 def run_copy_calibration(args, P, W):
     """A plain device-to-device copy of 1 GiB (torch's copy kernel): the known-size
     transfer that the HBM byte counters of the decode kernel are scaled by."""
@@ -887,6 +920,7 @@ def run_copy_calibration(args, P, W):
 WORKLOADS = {"llama8b-decode-step": run_llama8b, "mixed-append-fp8": run_mixed_append,
              "long-context": run_long_context, "packed3-decode": run_packed3,
              "pack3-exhaustive": run_pack3_exhaustive, "copy-calibration": run_copy_calibration,
+             "add-calibration": run_add_calibration,
              "fp8-decode": run_fp8_decode, "dual-stacked-decode": run_dual_stacked,
              "e5m2-decode": lambda a, P, W: run_fp8_decode(a, P, W, "e5m2"),
              "int8-decode": lambda a, P, W: run_fp8_decode(a, P, W, "i8"),
@@ -901,6 +935,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pad-frac", type=float, default=0.10)
     ap.add_argument("--workload", default="llama8b-decode-step", choices=sorted(WORKLOADS))
     args = ap.parse_args()
     if args.gpus != 1:

@@ -207,6 +207,12 @@ size_t paged_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads,
  *                    stream, or synchronised); overlapping calls on it race.
  *   batch            0 .. 8192.
  * Accumulation is fp32; outputs are rounded to q_dtype to nearest even.
+ * Reproducibility: results are fixed up to the order of the fp32 additions.  The token streams
+ * of a workgroup share a range's chunks at run time, and the workgroups that share a long
+ * segment share its blocks, so which wave sums which tokens, and in which order, depends on
+ * timing.  Two calls on the same inputs attend over the same tokens with the same weights and
+ * agree to within fp32 rounding of the sums (far inside the 2e-3 attention tolerance), not bit
+ * for bit.
  */
 int paged_decode(void* out, const void* q, pkv_dtype q_dtype,
                  int64_t q_stride_b, int64_t q_stride_h, int64_t o_stride_b, int64_t o_stride_h,

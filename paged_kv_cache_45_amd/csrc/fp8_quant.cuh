@@ -9,7 +9,10 @@
 // Two shortcuts keep this cheap on gfx950, both checked exhaustively against the plain
 // definitions (tests/gpu_kernels/fp8_checks.hip, run by tests/test_gpu_fp8_exhaustive.py):
 //  * the quotient x / s of a whole row comes from one correctly rounded reciprocal r = 1 / s
-//    and one fma correction per value, q = fma(fma(-s, x r, x), r, x r) with the sign of x.
+//    and one fma correction per value, q = fma(fma(-s, x r, x), r, x r) with the sign of x:
+//    the residual-correction step of Markstein's fma division (P. Markstein, IBM J. Res. Dev.
+//    34(1), 1990; J.-M. Muller et al., Handbook of Floating-Point Arithmetic, on division with
+//    an fma), here without the theorem's conditions on r and x r, hence the exhaustive check.
 //    q can differ from the correctly rounded x / s in its last bit, but for every 16-bit (fp16
 //    or bf16) x with |x| <= absmax and every 16-bit absmax, its e4m3 code is the code of the
 //    correctly rounded quotient.  Scales outside [2^-100, 2^100] (reciprocal overflow,
