@@ -507,11 +507,14 @@ def test_max_batch_ragged():
         assert report(f"max batch ps{ps}", got, want, wl.dtype) <= ATTN_TOL
 
 
-@pytest.mark.parametrize("G", [1, 8])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
 @pytest.mark.parametrize("D,bs", [(128, 16), (64, 64)])
 def test_u3_decode_shapes_ragged(G, D, bs):
     """3-bit pools (quantised and packed by the oracle, uploaded as they are) at group sizes and
-    head dims the full-size cases do not use; ragged and empty contexts, two partition sizes."""
+    head dims the full-size cases do not use; ragged and empty contexts, two partition sizes.
+    With 2 kv heads a wave instruction holds tokens of 2 heads, so these run the row-major
+    own-head form (its query-sum selection for 2 and 4 heads included); the matrix-core form at
+    8 kv heads is covered in test_gpu_mq_shapes.py."""
     P = need_gpu()
     Hkv = 2
     lens = [1, 15, 16, 17, 511, 512, 513, 1000, 0, 33]
