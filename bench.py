@@ -1,10 +1,12 @@
 """Benchmark of the paged KV-cache hot path on one MI355X.
 
 Default workload (the headline): one step = the whole path over one Llama-8B-shaped decode
-batch: kv_append of one new token per request (64 tokens, bf16, 8 kv heads of 128) into a
-paged pool (block size 16), then paged_decode of one query token per request (32 q heads,
+batch: the append of one new token per request (64 tokens, bf16, 8 kv heads of 128) into a
+paged pool (block size 16), then the decode of one query token per request (32 q heads,
 GQA 4) over the updated context (513..4097 tokens, U{512..4096} cached + 1), split-K
-ranges merged by log-sum-exp.  Inputs are synthetic, seeded, already resident in HBM.
+ranges merged by log-sum-exp.  The step is one paged_decode_append launch (the decode's
+workgroups write the new tokens), or with --separate-append kv_append then paged_decode.
+Inputs are synthetic, seeded, already resident in HBM.
 
 Four per-layer pools (same shapes and block tables, different data) are used in rotation,
 one per step, as in a multi-layer decode: between two reads of a pool ~1.8 GB of other
@@ -56,6 +58,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 N_LAYERS = 4
 METRIC = "paged decode KV GB/s (% of HBM peak) + append tokens/s, Llama-8B shape"
 DECODE_SOURCES = ("paged_kv_cache_45_amd/csrc/decode.hip", "paged_kv_cache_45_amd/csrc/decode_kernel.cuh",
+                  "paged_kv_cache_45_amd/csrc/append_rows.cuh",
                   "paged_kv_cache_45_amd/csrc/decode_same_d128.hip", "paged_kv_cache_45_amd/csrc/common.cuh",
                   "paged_kv_cache_45_amd/csrc/launch.h", "paged_kv_cache_45_amd/csrc/api.cpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama8b_hbm_traffic.md")
@@ -91,21 +94,19 @@ def sources_sha256():
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """HBM bytes per paged_decode launch from the committed counter summary, or None when
+def recorded_traffic(entry_point):
+    """HBM bytes per launch of `entry_point` from the committed counter summary, or None when
     there is none or the decode sources changed since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             text = f.read()
     except OSError:
         return None
-    m = re.search(r"^traffic-record: (\{.*\})$", text, re.M)
-    if not m:
-        return None
-    rec = json.loads(m.group(1))
-    if rec.get("sources_sha256") != sources_sha256():
-        return None
-    return int(rec["hbm_bytes_per_launch"])
+    for m in re.finditer(r"^traffic-record: (\{.*\})$", text, re.M):
+        rec = json.loads(m.group(1))
+        if rec.get("entry_point") == entry_point and rec.get("sources_sha256") == sources_sha256():
+            return int(rec["hbm_bytes_per_launch"])
+    return None
 
 
 # per-call statistics (the roofline figure among them) take the median of at least this many
@@ -171,8 +172,8 @@ def base_record(args, metric, value, unit, ms_per_step, dtype, config, higher=Tr
             "data": "synthetic", "config": config}
 
 
-def hbm_roofline(kernel, alg_bytes, ms, traffic=None):
-    """Roofline record of one entry point from its event-timed calls `ms` (milliseconds): the
+def hbm_roofline(kernel, alg_bytes, ms, traffic=None, timing="event-timed calls"):
+    """Roofline record of one entry point from its timed calls `ms` (milliseconds): the
     achieved rate is the algorithmic bytes over the median call duration; the mean and the
     20th/80th percentiles are reported beside it."""
     import numpy as np
@@ -181,7 +182,7 @@ def hbm_roofline(kernel, alg_bytes, ms, traffic=None):
     return {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "algorithmic_bytes": int(alg_bytes),
-            "statistic": f"median of {len(ms)} event-timed calls",
+            "statistic": f"median of {len(ms)} {timing}",
             "frac_of_mean": round(alg_bytes / (float(ms.mean()) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "frac_p20_p80": [round(alg_bytes / (float(np.quantile(ms, q)) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
                              for q in (0.8, 0.2)]}
@@ -335,9 +336,19 @@ def run_llama8b(args, P, W):
         P.paged_decode(w.q, w.k_pool, w.v_pool, d["bt"], d["ctx"], w.max_context_len, w.sm_scale,
                        partition_size=args.partition_size, workspace=d["ws"], out=d["out"])
 
+    def fused(i):
+        w, d = layers[i % N_LAYERS], dev[i % N_LAYERS]
+        P.paged_decode_append(w.q, w.new_k, w.new_v, w.k_pool, w.v_pool, d["bt"], d["ctx"], w.max_context_len,
+                              w.sm_scale, partition_size=args.partition_size, workspace=d["ws"], out=d["out"])
+
+    # the step: one paged_decode_append launch (the new tokens appended by the decode's own
+    # workgroups), or with --separate-append kv_append then paged_decode
     def step(i):
-        append(i)
-        decode(i)
+        if args.separate_append:
+            append(i)
+            decode(i)
+        else:
+            fused(i)
 
     for i in range(args.warmup):
         step(i)
@@ -379,6 +390,7 @@ def run_llama8b(args, P, W):
         assert bool(((e - r).abs() <= 2 * (2e-3 + half_ulp)).all()), "graph replay differs from eager"
 
     # per-entry-point durations with events on the launch stream
+    step_ms = None if args.separate_append else call_times_ms(fused, args, stream)
     dec_ms = call_times_ms(decode, args, stream)
     app_ms, _ = graph_call_times_ms([lambda i=i: append(i) for i in range(N_LAYERS)],
                                     max(1, args.steps // N_LAYERS))
@@ -392,18 +404,25 @@ def run_llama8b(args, P, W):
               "num_kv_heads": wl0.num_kv_heads, "head_dim": D, "block_size": wl0.block_size,
               "context": "U{512..4096} cached + 1 appended", "layers_rotated": N_LAYERS,
               "partition_size": args.partition_size or "auto",
+              "step": "kv_append + paged_decode" if args.separate_append else "paged_decode_append",
               "launch": "one HIP graph of the four layers' steps, replayed"}
     rec = base_record(args, METRIC, value, "GB/s", ms_per_step, "bf16", config)
     ds, aps = stats_us(dec_ms), stats_us(app_ms)
     rec.update({
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_us": ds, "decode_us_median": ds["median"], "decode_us_p20_p80": ds["p20_p80"],
+        "decode_timing": "paged_decode alone (over the appended pools), event-timed calls",
         "append_us_median": aps["median"],
         "append_tokens_per_s": round(B / (aps["median"] * 1e-6), 1),
-        "append_timing": "graph replay of the 4 per-layer appends (the kernel alone is launch-bound)",
-        "roofline": hbm_roofline("paged_decode (decode_kernel + merge_kernel)", dec_bytes_all,
-                                 dec_ms, recorded_traffic()),
+        "append_timing": "kv_append alone, graph replay of the 4 per-layer appends (launch-bound)",
     })
+    if args.separate_append:
+        rec["roofline"] = hbm_roofline("paged_decode (decode_kernel + merge_kernel)", dec_bytes_all,
+                                       dec_ms, recorded_traffic("paged_decode"))
+    else:
+        rec["step_us"] = stats_us(step_ms)
+        rec["roofline"] = hbm_roofline("paged_decode_append (decode_kernel with the step's append + merge_kernel)",
+                                       dec_bytes_all + app_b, step_ms, recorded_traffic("paged_decode_append"))
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl0, host_k, host_v)
     return rec
@@ -458,7 +477,7 @@ def run_mixed_append(args, P, W):
     rec = base_record(args, "append tokens/s (mixed prefill + decode, fp8 cache)",
                       valid / (st["median"] * 1e-6), "tokens/s", ms_per_step, "f32", config)
     rec.update({"append_us": st, "timing": f"graph replay of the {n_copies} rotated calls",
-                "roofline": hbm_roofline("append_kernel (fp8)", alg, ms)})
+                "roofline": hbm_roofline("append_kernel (fp8)", alg, ms, timing="per call from graph replays of the 8 rotated calls")})
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = append_cpu_baseline(wl, valid)
     return rec
@@ -936,6 +955,8 @@ def main():
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pad-frac", type=float, default=0.10)
+    ap.add_argument("--separate-append", action="store_true",
+                    help="Llama-8B step as kv_append then paged_decode instead of one paged_decode_append")
     ap.add_argument("--workload", default="llama8b-decode-step", choices=sorted(WORKLOADS))
     args = ap.parse_args()
     if args.gpus != 1:

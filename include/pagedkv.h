@@ -250,6 +250,41 @@ int paged_decode_scaled(void* out, const void* q, pkv_dtype q_dtype,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * paged_decode_append - one decode step in one launch: the new token of every request is
+ * appended to the cache, then the decode attends over the cache including it.
+ *
+ * Defined as kv_append of k_new / v_new ([Append], Required reasoning process steps 1-9) with
+ * request b's token at slot block_tables[b, pos / block_size] * block_size + pos % block_size,
+ * pos = context_lens[b] - 1 (the slot construction of step 9 for a decode token; no token for a
+ * request with context_lens[b] == 0), followed by paged_decode ([Paged], Step 1 and TODO 1-5)
+ * with the same context_lens: the same pool contents (bit for bit) and the same outputs as those
+ * two calls.  The workgroup of the decode that reads a request's last token writes that token
+ * first, so nothing else is launched for the append.
+ *   k_new, v_new     device [batch, num_kv_heads, head_dim] of q_dtype, element (b, h, d) at
+ *                    b*stride_b + h*stride_h + d (strides >= 0, multiples of 8; 16-byte
+ *                    aligned), read only.
+ *   k_cache, v_cache, k_meta, v_meta  as for kv_append (written: the new rows, and for the
+ *                    quantised caches their per-row scales or (s, z) pairs, computed as kv_append
+ *                    computes them) and for paged_decode (read).
+ *   other arguments  as for paged_decode.  The context lengths count the new token.
+ * A block id outside [0, num_blocks) skips that request's write, as kv_append skips a slot
+ * outside the pool.  Long segments are not handed out at run time in this call (every segment's
+ * last token must have one reader), so the split is static.  The workspace is shared with
+ * paged_decode (same size query).
+ */
+int paged_decode_append(void* out, const void* q, pkv_dtype q_dtype,
+                        int64_t q_stride_b, int64_t q_stride_h, int64_t o_stride_b, int64_t o_stride_h,
+                        const void* k_new, const void* v_new, int64_t k_new_stride_b, int64_t k_new_stride_h,
+                        int64_t v_new_stride_b, int64_t v_new_stride_h,
+                        void* k_cache, void* v_cache, pkv_dtype cache_dtype,
+                        int64_t c_stride_block, int64_t c_stride_slot, int64_t c_stride_head,
+                        void* k_meta, void* v_meta,
+                        const int32_t* block_tables, int64_t bt_stride_b, const int32_t* context_lens,
+                        int batch, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                        int64_t num_blocks, int max_context_len, float sm_scale, int partition_size,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * paged_decode_noalloc - paged_decode for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid allocation).
  *

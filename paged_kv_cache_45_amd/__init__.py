@@ -7,7 +7,7 @@ in the HIP kernels.  There is no fallback: if the library is missing or a call f
 an exception is raised.
 
 Entry points (same names as the C ABI):
-    kv_append, kv_append_scaled, paged_decode, paged_decode_scaled, paged_decode_noalloc,
+    kv_append, kv_append_scaled, paged_decode, paged_decode_scaled, paged_decode_append, paged_decode_noalloc,
     paged_decode_workspace_size, build_slot_mapping, pack3, unpack3, pkv_status_string
 """
 from __future__ import annotations
@@ -17,7 +17,8 @@ import math
 import os
 from typing import Optional
 
-__all__ = ["kv_append", "kv_append_scaled", "paged_decode", "paged_decode_scaled", "paged_decode_noalloc",
+__all__ = ["kv_append", "kv_append_scaled", "paged_decode", "paged_decode_scaled", "paged_decode_append",
+           "paged_decode_noalloc",
            "build_slot_mapping", "paged_decode_workspace_size", "pack3", "unpack3",
            "pkv_status_string", "decode_workspace", "library_path", "load_library",
            "PKV_F16", "PKV_BF16", "PKV_FP8_E4M3FN", "PKV_U3", "PKV_FP8_E5M2", "PKV_INT8",
@@ -69,6 +70,10 @@ def load_library() -> ctypes.CDLL:
     lib.paged_decode_scaled.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, vp, i32, i64, i64, i64,
                                         vp, vp, i64, i64, i64, vp, i64, vp, i32, i32, i32, i32, i32,
                                         i64, i32, f32, i32, vp, sz, vp]
+    lib.paged_decode_append.restype = i32
+    lib.paged_decode_append.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, vp, i64, i64, i64, i64,
+                                        vp, vp, i32, i64, i64, i64, vp, vp, vp, i64, vp, i32, i32, i32,
+                                        i32, i32, i64, i32, f32, i32, vp, sz, vp]
     lib.paged_decode_noalloc.restype = i32
     lib.paged_decode_noalloc.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, vp, i32, i64, i64, i64,
                                          vp, vp, vp, i64, vp, i32, i32, i32, i32, i32, i64, i32, f32,
@@ -230,6 +235,44 @@ def paged_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_le
     else:
         st = load_library().paged_decode(*head, *tail)
         _check("paged_decode", st)
+    return out
+
+
+def paged_decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
+                        max_context_len: int, sm_scale: Optional[float] = None, k_meta=None,
+                        v_meta=None, partition_size: int = 0, workspace=None, out=None,
+                        cache_dtype=None, stream=None):
+    """One decode step in one launch: k_new / v_new [B, Hkv, D] (q's dtype) appended at position
+    context_lens[b] - 1 of each request (the slot from its block table; none where the length is
+    0), then paged_decode over context_lens (which count the new token)."""
+    import torch
+    qdt = _dtype16(q)
+    if q.dim() != 3 or q.stride(2) != 1:
+        raise ValueError("q must be [B, Hq, D] with unit stride on D")
+    B, Hq, D = q.shape
+    for t in (k_new, v_new):
+        if t.dim() != 3 or t.stride(2) != 1 or t.dtype != q.dtype or tuple(t.shape) != (B, k_cache.shape[2], D):
+            raise ValueError("k_new / v_new must be [B, Hkv, D] of q's dtype with unit stride on D")
+    cdt = _cache_dtype(k_cache, qdt, cache_dtype)
+    sb, ss, sh = _cache_strides(k_cache, v_cache)
+    if out is None:
+        out = torch.empty_like(q)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    if block_tables.dim() != 2 or block_tables.stride(1) != 1:
+        raise ValueError("block_tables must be [B, max_blocks] with unit stride")
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, k_cache.shape[2], D, max_context_len, partition_size,
+                                     q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().paged_decode_append(
+        _ptr(out), _ptr(q), qdt, q.stride(0), q.stride(1), out.stride(0), out.stride(1),
+        _ptr(k_new), _ptr(v_new), k_new.stride(0), k_new.stride(1), v_new.stride(0), v_new.stride(1),
+        _ptr(k_cache), _ptr(v_cache), cdt, sb, ss, sh, _ptr(k_meta), _ptr(v_meta),
+        _ptr(block_tables), block_tables.stride(0), _ptr(context_lens), B, Hq, k_cache.shape[2], D,
+        k_cache.shape[1], k_cache.shape[0], int(max_context_len), float(sm_scale),
+        int(partition_size), _ptr(workspace), wbytes, _stream(stream))
+    _check("paged_decode_append", st)
     return out
 
 

@@ -290,7 +290,16 @@ size_t paged_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads,
   return decode_layout(batch, num_q_heads, num_kv_heads, head_dim, max_context_len, ps, -1, -1).bytes;
 }
 
-// paged_decode and paged_decode_scaled; meta entry of row (blk, slot, head) as for append_impl.
+// The new K and V rows of a fused decode step (paged_decode_append): [batch, num_kv_heads,
+// head_dim] of the query dtype, element strides.
+struct NewRows {
+  const void* k;
+  const void* v;
+  int64_t k_sb, k_sh, v_sb, v_sh;
+};
+
+// paged_decode, paged_decode_scaled and paged_decode_append (new rows given); meta entry of row
+// (blk, slot, head) as for append_impl.
 static int decode_impl(void* out, const void* q, pkv_dtype q_dtype,
                        int64_t q_stride_b, int64_t q_stride_h, int64_t o_stride_b, int64_t o_stride_h,
                        const void* k_cache, const void* v_cache, pkv_dtype cache_dtype,
@@ -300,8 +309,14 @@ static int decode_impl(void* out, const void* q, pkv_dtype q_dtype,
                        int batch, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                        int64_t num_blocks, int max_context_len, float sm_scale, int partition_size,
                        void* workspace, size_t workspace_bytes, hipStream_t stream,
-                       int64_t m_sb, int64_t m_ss, int64_t m_sh) {
+                       int64_t m_sb, int64_t m_ss, int64_t m_sh, const NewRows* nr = nullptr) {
   if (!known(q_dtype) || !known(cache_dtype)) return PKV_EINVAL;
+  if (nr) {                            // the fused append's new rows: 16-byte rows of the query dtype
+    if (!nr->k || !nr->v || !aligned(nr->k, 16) || !aligned(nr->v, 16)) return PKV_EINVAL;
+    if (nr->k_sb < 0 || nr->k_sh < 0 || nr->v_sb < 0 || nr->v_sh < 0 || nr->k_sb % 8 || nr->k_sh % 8 ||
+        nr->v_sb % 8 || nr->v_sh % 8)
+      return PKV_EINVAL;
+  }
   if (m_sb < 0 || m_ss < 0 || m_sh < 0) return PKV_EINVAL;
   if (!is16(q_dtype)) return PKV_EUNSUPPORTED;
   if (is16(cache_dtype) && cache_dtype != q_dtype) return PKV_EINVAL;
@@ -413,6 +428,17 @@ static int decode_impl(void* out, const void* q, pkv_dtype q_dtype,
                    L.plan.heads_per_group / L.plan.hpi <= kClaimCounters) ? 1 : 0;
   p.log2_claim = 0;
   while ((1 << p.log2_claim) < unit_tokens) ++p.log2_claim;
+  if (nr) {
+    // the fused append needs the one reader of each request's last token to be the workgroup
+    // holding its last granule: no run-time hand-out, whose units any sharer may take
+    p.claim_units = 0;
+    p.k_new = nr->k;
+    p.v_new = nr->v;
+    p.kn_sb = nr->k_sb;
+    p.kn_sh = nr->k_sh;
+    p.vn_sb = nr->v_sb;
+    p.vn_sh = nr->v_sh;
+  }
   const SplitWeights sw = p.claim_units ? kSplitClaimed : cache_dtype == PKV_U3 ? kSplitStaticU3 : kSplitStatic;
   p.split_w[0] = sw.first_even;
   p.split_w[1] = sw.first_odd;
@@ -456,6 +482,26 @@ int paged_decode_scaled(void* out, const void* q, pkv_dtype q_dtype,
                      block_tables, bt_stride_b, context_lens, batch, num_q_heads, num_kv_heads,
                      head_dim, block_size, num_blocks, max_context_len, sm_scale, partition_size,
                      workspace, workspace_bytes, stream, s_stride_block, s_stride_slot, s_stride_head);
+}
+
+int paged_decode_append(void* out, const void* q, pkv_dtype q_dtype,
+                        int64_t q_stride_b, int64_t q_stride_h, int64_t o_stride_b, int64_t o_stride_h,
+                        const void* k_new, const void* v_new, int64_t k_new_stride_b, int64_t k_new_stride_h,
+                        int64_t v_new_stride_b, int64_t v_new_stride_h,
+                        void* k_cache, void* v_cache, pkv_dtype cache_dtype,
+                        int64_t c_stride_block, int64_t c_stride_slot, int64_t c_stride_head,
+                        void* k_meta, void* v_meta,
+                        const int32_t* block_tables, int64_t bt_stride_b, const int32_t* context_lens,
+                        int batch, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                        int64_t num_blocks, int max_context_len, float sm_scale, int partition_size,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const NewRows nr{k_new, v_new, k_new_stride_b, k_new_stride_h, v_new_stride_b, v_new_stride_h};
+  return decode_impl(out, q, q_dtype, q_stride_b, q_stride_h, o_stride_b, o_stride_h, k_cache, v_cache,
+                     cache_dtype, c_stride_block, c_stride_slot, c_stride_head, k_meta, v_meta,
+                     block_tables, bt_stride_b, context_lens, batch, num_q_heads, num_kv_heads,
+                     head_dim, block_size, num_blocks, max_context_len, sm_scale, partition_size,
+                     workspace, workspace_bytes, stream, (int64_t)block_size * num_kv_heads,
+                     num_kv_heads, 1, &nr);
 }
 
 }  // extern "C"

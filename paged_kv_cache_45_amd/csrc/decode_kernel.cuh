@@ -48,6 +48,7 @@
 #include "launch.h"
 #include "common.cuh"
 #include "fp8_quant.cuh"
+#include "append_rows.cuh"
 
 namespace pkv {
 
@@ -735,17 +736,36 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
   }
 }
 
+// A wave that stored appended rows: once its stores have completed (s_waitcnt 0, which also waits
+// for its loads in flight), count it in `done` (LDS).
+__device__ __forceinline__ void count_appended(int* done) {
+  __builtin_amdgcn_s_waitcnt(0);
+  if ((threadIdx.x & 63) == 0) {
+    typedef __attribute__((address_space(3))) int LdsInt;
+    __hip_atomic_fetch_add((LdsInt*)done, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+}
+// Wait until `done` (LDS) reaches `target`: the rows this workgroup appended (append_new_rows) are in memory.
+__device__ __forceinline__ void wait_appended(int* done, int target) {
+  typedef __attribute__((address_space(3))) int LdsInt;
+  while (__hip_atomic_load((LdsInt*)done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < target)
+    __builtin_amdgcn_s_sleep(1);
+}
+
 // Reduce the chunks of tokens [t0, t1) of request b, head group hg into S (this lane's row:
 // head hh of the group, token offset tr inside a wave instruction).  The token streams of one
 // head wave take the chunks from a counter in LDS (`cnt`, zero at the start) rather than a
 // fixed interleave, so that a wave that streams faster (the SIMD issues the oldest waves
 // first) takes more chunks and the workgroup's waves finish the range together.  Physical
 // block ids of up to 64 blocks are fetched with one vector load (lane j <-> j-th block of the
-// window) and read back with v_readlane; the next chunk's K/V loads are issued before the
-// current chunk is computed (two register buffers).
+// window) and read back with v_readlane; the K/V loads of the next chunks are issued before the
+// current chunk is computed (a ring of register buffers).  With a fused append (new_tok >= 0) the
+// chunk holding the appended token is loaded only once the workgroup's stores of it are counted.
 template <int D, int G, bool BF16, CacheKind KIND, int HPI>
 __device__ __forceinline__ void run_range(const DecodeParams& p, State<G>& S, int b, int hg, int t0,
-                                                 int t1, int lane, int tr, int hh, int c, int* cnt) {
+                                                 int t1, int lane, int tr, int hh, int c, int* cnt,
+                                                 int new_tok = -1, int* app_done = nullptr, int app_target = 0,
+                                                 bool app_mine = false) {
   using Gm = Geo<D, HPI, G>;
   using R = Regs<Gm::NI, KIND>;
   constexpr int esz = KIND == CacheKind::U3 ? 4 : byte_kind(KIND) ? 1 : 2;
@@ -791,6 +811,15 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, State<G>& S, in
       return;
     }
     const int tok0 = t0 + k * Gm::CT;
+    // the chunk holding a token this workgroup appended: its rows must be in memory first (a
+    // storing wave counts its own stores before it waits, so it never waits for itself)
+    if (live && new_tok >= tok0 && new_tok < tok0 + Gm::CT) {
+      if (app_mine) {
+        count_appended(app_done);
+        app_mine = false;
+      }
+      wait_appended(app_done, app_target);
+    }
     const int64_t slot0 = tok0 & (p.block_size - 1);
     const int64_t rowb = (phys * p.c_sb + slot0 * p.c_ss) * esz;
     const int64_t metab = (phys * p.m_sb + slot0 * p.m_ss) * 4;
@@ -825,6 +854,7 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, State<G>& S, in
     raw = claim_raw();
     issue(kq[b], r[b], kq[b] < n_plain);
   }
+
   bool done = kq[0] >= n_plain;
   while (!done) {
 #pragma unroll
@@ -837,12 +867,17 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, State<G>& S, in
       // would then wait for all loads in flight before the next chunk's are even issued
       __builtin_amdgcn_sched_barrier(0);
       compute_chunk<D, G, BF16, KIND, HPI, false>(p, S, r[b], tok_of(kq[b]), t1, c);
+      if (app_mine) {                    // this wave stored appended rows: count them, one chunk on
+        count_appended(app_done);
+        app_mine = false;
+      }
       if (kq[(b + 1) % NB] >= n_plain) {
         done = true;
         break;
       }
     }
   }
+  if (app_mine) count_appended(app_done);   // a range that ended before the first computed chunk
   if (ragged && k_end == n_plain) {      // the ragged last chunk, taken by exactly one wave
     R regs;
     issue(n_plain, regs, true);
@@ -1004,6 +1039,42 @@ __device__ __forceinline__ void store_out_row(const DecodeParams& p, int b, int 
   *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + b * p.o_sb + (int64_t)h * p.o_sh + c * 8) = o;
 }
 
+// The fused append of a decode step ("Write Triton Kv Cache Append Kernel", Required reasoning
+// process steps 4-9, with the slot of request b's new token taken from its block table as step 9
+// builds it: block_tables[b, pos / block_size] * block_size + pos % block_size, pos =
+// context_lens[b] - 1): the new K and V rows of the group's heads, converted to the cache's format
+// as kv_append converts them (append_rows.cuh).  A block id outside the pool skips the write, as
+// kv_append skips a slot outside the pool.  Called by the one workgroup that reads that token.
+// The rows are loaded together with the block id (one load latency).  Each wave that holds rows
+// later waits for its own stores to complete and counts itself done in an LDS counter (in
+// run_range, after its first computed chunk, by when the stores have long completed); the wave
+// that loads the chunk holding the new token waits for that count first (wait_appended), so no
+// other wave waits and no barrier is needed.  Returns the number of waves that store.
+template <int D, bool BF16, CacheKind KIND>
+__device__ __forceinline__ int append_new_rows(const DecodeParams& p, int b, int hg, int ctx) {
+  constexpr int LPR = D / 8;
+  constexpr int RPW = 64 / LPR;                          // rows per wave
+  const int pos = ctx - 1;
+  const int e = p.block_tables[(int64_t)b * p.bt_sb + (pos >> p.log2_bs)];
+  const int64_t off = pos & (p.block_size - 1);
+  const int c = threadIdx.x % LPR;
+  const int nwaves = blockDim.x >> 6;
+  const int storing = min(nwaves, (p.heads_per_group + RPW - 1) / RPW);
+  for (int r = threadIdx.x / LPR; r < p.heads_per_group; r += blockDim.x / LPR) {
+    const int h = hg * p.heads_per_group + r;
+    const uint4 kx = load_stream_u4(static_cast<const uint16_t*>(p.k_new) + b * p.kn_sb + (int64_t)h * p.kn_sh + c * 8);
+    const uint4 vx = load_stream_u4(static_cast<const uint16_t*>(p.v_new) + b * p.vn_sb + (int64_t)h * p.vn_sh + c * 8);
+    if (e >= 0 && e < p.num_blocks) {                   // the same value in every lane
+      const int64_t crow = (int64_t)e * p.c_sb + off * p.c_ss + (int64_t)h * p.c_sh;
+      const int64_t mrow = (int64_t)e * p.m_sb + off * p.m_ss + (int64_t)h * p.m_sh;
+      store_kv_row<LPR, BF16, KIND>(kx, vx, const_cast<void*>(p.k_cache), const_cast<void*>(p.v_cache),
+                                    const_cast<void*>(p.k_meta), const_cast<void*>(p.v_meta), crow, mrow, c,
+                                    false);
+    }
+  }
+  return storing;
+}
+
 // CLAIM: compiled with the run-time hand-out of shared segments (p.claim_units set).
 // Kept out of the other instances so that its extra live state costs them no registers.
 template <int D, int G, bool BF16, CacheKind KIND, int HPI, bool CLAIM>
@@ -1014,7 +1085,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
   // chunk counters of the head waves' token streams, one set per segment parity: the set of
   // segment i + 1 is cleared during segment i, after the barriers that end segment i - 1
   __shared__ int s_cnt[2][kMaxWaves];
+  // waves whose rows of a fused append have reached memory (counts up over the segments)
+  __shared__ int s_app_done;
   if (threadIdx.x < 2 * kMaxWaves) s_cnt[threadIdx.x / kMaxWaves][threadIdx.x % kMaxWaves] = 0;
+  if (threadIdx.x == 0) s_app_done = 0;
   build_prefix(p, s_pref, s_tile);             // (ends with a barrier)
 
   const int lane = threadIdx.x & 63;
@@ -1042,6 +1116,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
   }
   bool first = true;
   int seg_i = 0;
+  int app_target = 0;                           // s_app_done once this workgroup's appends are in
   while (x < x_end) {
     // segment (request b, head group hg) holding unit x: the last b with NHG*s_pref[b] <= x
     int lo = 0, hi = p.batch;
@@ -1137,8 +1212,20 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
     }
     if (seg_i > 0 && threadIdx.x < kMaxWaves) s_cnt[(seg_i + 1) & 1][threadIdx.x] = 0;
     int* cnt = &s_cnt[seg_i & 1][wv];
+    int new_tok = -1;
+    bool app_mine = false;                      // this wave stored rows of this segment's append
+    if (p.k_new != nullptr && g1 == n) {
+      // fused append: this workgroup holds the segment's last granule, so it alone reads the new
+      // token, at position ctx - 1; the wave that loads it waits for the rows (append_new_rows)
+      const int storing = append_new_rows<D, BF16, KIND>(p, b, hg, ctx);
+      app_target += storing;
+      app_mine = (int)(threadIdx.x >> 6) < storing;
+      new_tok = ctx - 1;
+    }
     auto range = [&](int ta, int tb) {
-      run_range<D, G, BF16, KIND, HPI>(p, S, b, hg, ta, tb, lane, tr, hh, c, cnt);
+      run_range<D, G, BF16, KIND, HPI>(p, S, b, hg, ta, tb, lane, tr, hh, c, cnt, new_tok, &s_app_done,
+                                       app_target, app_mine);
+      app_mine = false;
     };
     if constexpr (CLAIM) {
       if (!(g0 == 0 && g1 == n)) {

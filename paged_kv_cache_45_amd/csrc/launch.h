@@ -64,6 +64,12 @@ struct DecodeParams {
   int* ws_claim;                      // [batch, head groups, 4] unit counters (cleared by each call)
   int claim_units;                    // shared segments hand out their tokens dynamically ...
   int log2_claim;                     // ... in units of 2^log2_claim tokens inside one block
+  // fused append of a decode step (paged_decode_append): request b's new K and V rows,
+  // [batch, num_kv_heads, head_dim] of the query dtype, are written at position
+  // context_lens[b] - 1 before the decode reads it; nullptr: no append
+  const void* k_new;
+  const void* v_new;
+  int64_t kn_sb, kn_sh, vn_sb, vn_sh; // elements
 };
 
 struct SlotParams {
