@@ -169,7 +169,7 @@ template <int G> constexpr int own_heads() { return G == 8 ? 2 : 1; }
 // query head n - the own-head layout (lane q holds head q) with the chunk's tokens in its
 // registers.  To feed it, the K loads are token-transposed: lane n of every quad reads token n,
 // and the chunk's 4 load instructions walk 4 slices of the head dim (lane of quad cq of a row,
-// instruction i: elements 8 j .. 8 j + 7 with j = i * (LPR / 4) + cq).  The quads of a row hold
+// instruction i: elements 8 j .. 8 j + 7 with j = mq_slice(i, cq)).  The quads of a row hold
 // partial sums over disjoint slices and are summed once per chunk.  V keeps the row-major
 // mapping (instruction i = token i).  With 8 query heads per kv head a second block set takes
 // heads 4 .. 7; with 2, columns 2 and 3 repeat heads 0 and 1.  This replaces the 4 G dot2 products
@@ -177,6 +177,15 @@ template <int G> constexpr int own_heads() { return G == 8 ? 2 : 1; }
 // load instruction and one row sum per chunk.
 template <int D, int G, int HPI>
 constexpr bool mq_form() { return own_head_form<D, G>() && Geo<D, HPI, G>::TPI == 1; }
+// The head-dim slice (8 elements) that instruction i of a chunk gives the lane of quad cq of a
+// row in the matrix-core form: i * (LPR / 4) + cq.  Byte codes pair the slices instead (slices
+// 2 j and 2 j + 1, j = (i / 2) * (LPR / 4) + cq, for instructions i and i + 1), so that one
+// 16-byte K load feeds two instructions: half the K load instructions of 8-byte loads, which is
+// what limits the byte-code decodes (a loads-only copy of the kernel is as slow as the full one).
+template <int LPR, CacheKind KIND>
+__device__ __forceinline__ constexpr int mq_slice(int i, int cq) {
+  return byte_kind(KIND) ? 2 * ((i >> 1) * (LPR / 4) + cq) + (i & 1) : i * (LPR / 4) + cq;
+}
 
 // Chunks whose loads are in flight at once per wave in the static-split loop (register buffers,
 // one being computed).  The 16-bit caches move 8 KB per wave per chunk and saturate the memory
@@ -329,7 +338,7 @@ __device__ __forceinline__ LaneOffsets<D, HPI, KIND, G> lane_offsets(const Decod
     const int64_t krow0 = (int64_t)n * p.c_ss + (int64_t)hh * p.c_sh;
 #pragma unroll
     for (int i = 0; i < Gm::NI; ++i) {
-      const int j = i * (Gm::LPR / 4) + cq;            // the lane's 8-element slice of the head dim
+      const int j = mq_slice<Gm::LPR, KIND>(i, cq);    // the lane's 8-element slice of the head dim
       if constexpr (KIND == CacheKind::U3) {
         // octet j = stream bits [24 j, 24 j + 24): starts at byte 3 j, in word 3 j / 4, and
         // spills into the next word for j mod 4 in {1, 2}
@@ -384,11 +393,15 @@ __device__ __forceinline__ void load_chunk(const DecodeParams& p, const char* kb
       const BufRsrc kmr = buf_rsrc(kmb, nrec), vmr = buf_rsrc(vmb, nrec);
       R.ks[0] = __uint_as_float(buf_load_u32<false>(kmr, o.mrow, 0));
       R.vs[0] = __uint_as_float(buf_load_u32<false>(vmr, o.mrow, 0));
+      static_assert(Gm::NI % 2 == 0, "paired K slices");
 #pragma unroll
-      for (int i = 0; i < Gm::NI; ++i) {
-        R.k[i] = buf_load_u2<false>(kr, o.krow[i], 0);
-        R.v[i] = buf_load_u2<true>(vr, o.vrow, i * ss);
+      for (int i = 0; i < Gm::NI; i += 2) {            // slices of instructions i, i + 1: one load
+        const uint4 k2 = buf_load_u4<false>(kr, o.krow[i], 0);
+        R.k[i] = make_uint2(k2.x, k2.y);
+        R.k[i + 1] = make_uint2(k2.z, k2.w);
       }
+#pragma unroll
+      for (int i = 0; i < Gm::NI; ++i) R.v[i] = buf_load_u2<true>(vr, o.vrow, i * ss);
     } else {
       const BufRsrc kmr = buf_rsrc(kmb, nrec), vmr = buf_rsrc(vmb, nrec);
       R.km[0] = buf_load_u32<true>(kmr, o.mrow, 0);          // (s, z) of token lane mod 4
@@ -1192,7 +1205,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
         float qs = 0.f;
 #pragma unroll
         for (int i = 0; i < Gm::NI; ++i) {
-          const int j = i * (Gm::LPR / 4) + (c >> 2);
+          const int j = mq_slice<Gm::LPR, KIND>(i, c >> 2);
           const uint4 v = *reinterpret_cast<const uint4*>(q_row + (int64_t)g * p.q_sh + j * 8);
           if constexpr (KIND == CacheKind::U3) {
             S.qm[hs][i][0] = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
