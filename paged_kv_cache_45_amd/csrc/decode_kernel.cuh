@@ -178,13 +178,23 @@ template <int G> constexpr int own_heads() { return G == 8 ? 2 : 1; }
 template <int D, int G, int HPI>
 constexpr bool mq_form() { return own_head_form<D, G>() && Geo<D, HPI, G>::TPI == 1; }
 // The head-dim slice (8 elements) that instruction i of a chunk gives the lane of quad cq of a
-// row in the matrix-core form: i * (LPR / 4) + cq.  Byte codes pair the slices instead (slices
-// 2 j and 2 j + 1, j = (i / 2) * (LPR / 4) + cq, for instructions i and i + 1), so that one
-// 16-byte K load feeds two instructions: half the K load instructions of 8-byte loads, which is
-// what limits the byte-code decodes (a loads-only copy of the kernel is as slow as the full one).
+// row in the matrix-core form: i * (LPR / 4) + cq for 16-bit caches.  The coded caches pair the
+// slices instead (slices 2 j and 2 j + 1, j = (i / 2) * (LPR / 4) + cq, for instructions i and
+// i + 1), so that one K load feeds two instructions: byte codes one 16-byte load instead of two
+// 8-byte ones (the byte-code decodes are bound by their load stream: a loads-only copy of the
+// kernel is as slow as the full one), 3-bit codes one 8-byte load instead of four 4-byte ones
+// (the 6 bytes of two octets always lie in two aligned words).
 template <int LPR, CacheKind KIND>
 __device__ __forceinline__ constexpr int mq_slice(int i, int cq) {
-  return byte_kind(KIND) ? 2 * ((i >> 1) * (LPR / 4) + cq) + (i & 1) : i * (LPR / 4) + cq;
+  return KIND != CacheKind::Same ? 2 * ((i >> 1) * (LPR / 4) + cq) + (i & 1) : i * (LPR / 4) + cq;
+}
+// 3-bit codes, matrix-core form: the byte permute that lines octet j up from the 8 bytes of the
+// word pair holding octets j & ~1 and (j & ~1) + 1 (they start at byte (3 (j & ~1)) mod 4, which
+// is 0 or 2, and octet j + 1 three bytes later), arranged for the packed 16-bit shifts (bytes
+// o, o + 1 in the low half, o + 1, o + 2 in the high half)
+__device__ __forceinline__ uint32_t u3_pair_sel(int j) {
+  const uint32_t o = (uint32_t)((3 * (j & ~1)) & 3) + 3u * (uint32_t)(j & 1);
+  return o * 0x01010101u + 0x02010100u;
 }
 
 // Chunks whose loads are in flight at once per wave in the static-split loop (register buffers,
@@ -312,10 +322,10 @@ struct LaneOffsets {
   static constexpr int NI = Geo<D, HPI, G>::NI;
   uint32_t row[NI];                  // bytes from the chunk's uniform row base
   uint32_t meta[NI];                 // u3: bytes from the chunk's uniform meta base
-  // matrix-core score form: the K rows of load instruction i (token-transposed; 3-bit: the word
-  // holding the start of the lane's octet, the next word or the same one again, and the byte
-  // permute that lines the octet up); V and meta of token 0 (token i adds i slot strides)
-  uint32_t krow[NI], krow_hi[NI], ksel[NI];
+  // matrix-core score form: the K rows of load instruction i (token-transposed; the coded
+  // caches load at even i the slices of instructions i and i + 1; 3-bit: the first of the two
+  // words that hold the lane's octet pair); V and meta of token 0 (token i adds i slot strides)
+  uint32_t krow[NI];
   uint32_t vrow, vrow_hi;
   uint32_t mrow;                     // meta of token (lane mod 4) of the chunk, the lane's head
 };
@@ -340,16 +350,11 @@ __device__ __forceinline__ LaneOffsets<D, HPI, KIND, G> lane_offsets(const Decod
     for (int i = 0; i < Gm::NI; ++i) {
       const int j = mq_slice<Gm::LPR, KIND>(i, cq);    // the lane's 8-element slice of the head dim
       if constexpr (KIND == CacheKind::U3) {
-        // octet j = stream bits [24 j, 24 j + 24): starts at byte 3 j, in word 3 j / 4, and
-        // spills into the next word for j mod 4 in {1, 2}
-        const bool two = ((j & 3) == 1) || ((j & 3) == 2);
-        o.krow[i] = (uint32_t)((krow0 + ((3 * j) >> 2)) * 4);
-        o.krow_hi[i] = o.krow[i] + (two ? 4u : 0u);
-        o.ksel[i] = (uint32_t)((3 * j) & 3) * 0x01010101u + 0x02010100u;
+        // octet j = stream bits [24 j, 24 j + 24): octets j & ~1 and its successor fill bytes
+        // [3 (j & ~1), 3 (j & ~1) + 6), inside words 3 (j & ~1) / 4 and the next one
+        o.krow[i] = (uint32_t)((krow0 + ((3 * (j & ~1)) >> 2)) * 4);
       } else {
         o.krow[i] = (uint32_t)((krow0 + 8 * j) * esz);
-        o.krow_hi[i] = 0;
-        o.ksel[i] = 0;
       }
     }
     const bool vtwo = ((c & 3) == 1) || ((c & 3) == 2);
@@ -407,9 +412,13 @@ __device__ __forceinline__ void load_chunk(const DecodeParams& p, const char* kb
       R.km[0] = buf_load_u32<true>(kmr, o.mrow, 0);          // (s, z) of token lane mod 4
       R.vm[0] = buf_load_u32<true>(vmr, o.mrow, 0);
 #pragma unroll
+      for (int i = 0; i < Gm::NI; i += 2) {            // octets of instructions i, i + 1: one load
+        const uint2 kw = buf_load_u2<false>(kr, o.krow[i], 0);
+        R.klo[i] = R.klo[i + 1] = kw.x;
+        R.khi[i] = R.khi[i + 1] = kw.y;
+      }
+#pragma unroll
       for (int i = 0; i < Gm::NI; ++i) {
-        R.klo[i] = buf_load_u32<false>(kr, o.krow[i], 0);
-        R.khi[i] = buf_load_u32<false>(kr, o.krow_hi[i], 0);
         R.vlo[i] = buf_load_u32<true>(vr, o.vrow, i * ss);
         R.vhi[i] = buf_load_u32<true>(vr, o.vrow_hi, i * ss);
       }
@@ -495,11 +504,9 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
         kw[2] = codes2_to_16<KIND, BF16, false>(R.k[i].y);
         kw[3] = codes2_to_16<KIND, BF16, true>(R.k[i].y);
       } else {
-        // octet j of the row starts at byte (3 j) mod 4 of (klo, khi): the permute and the
+        // octet j of the row from the word pair (klo, khi) that holds it: the permute and the
         // packed shifts of the row-major form, pairs (code e, code e + 4)
-        const int j = i * (LPR / 4) + (c >> 2);
-        const uint32_t y = __builtin_amdgcn_perm(R.khi[i], R.klo[i],
-                                                 (uint32_t)((3 * j) & 3) * 0x01010101u + 0x02010100u);
+        const uint32_t y = __builtin_amdgcn_perm(R.khi[i], R.klo[i], u3_pair_sel(mq_slice<LPR, KIND>(i, c >> 2)));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const u16x2_t sh2 = {(uint16_t)(3 * e), (uint16_t)(3 * e + 4)};
