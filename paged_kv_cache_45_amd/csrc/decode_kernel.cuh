@@ -53,7 +53,7 @@
 namespace pkv {
 
 #ifndef PKV_PREFETCH_DEPTH
-#define PKV_PREFETCH_DEPTH 3
+#define PKV_PREFETCH_DEPTH 2
 #endif
 
 constexpr int kMaxWaves = 8;        // waves per workgroup at most (token streams x head group)
@@ -199,8 +199,10 @@ __device__ __forceinline__ uint32_t u3_pair_sel(int j) {
 
 // Chunks whose loads are in flight at once per wave in the static-split loop (register buffers,
 // one being computed).  The 16-bit caches move 8 KB per wave per chunk and saturate the memory
-// path with two buffers (a third measured 1.5 % slower); the byte-code and 3-bit caches move
-// 2.1 KB and 1.7 KB, and with two buffers are bound by load latency, not bandwidth.
+// path with two buffers (a third measured 1.5 % slower).  The byte-code and 3-bit caches move
+// 2.1 KB and 1.7 KB; with 8-byte K loads (4 per chunk) they were faster with three buffers, and
+// with the paired K loads (mq_slice: 2 per chunk) two are faster again (fp8 decode 0.534 -> 0.544
+// of 8 TB/s, 3-bit decode 0.263 -> 0.272, 28 and 20 fewer VGPRs; four: slower).
 template <int D, int G, CacheKind KIND, int HPI>
 constexpr int prefetch_depth() {
   if constexpr (KIND == CacheKind::Same || !mq_form<D, G, HPI>() || G == 8) return 2;
