@@ -1,11 +1,12 @@
-"""HIP-graph capture of one decode step (kv_append + paged_decode) at a padded maximum batch.
+"""HIP-graph capture of one decode step at a padded maximum batch: kv_append + paged_decode, and
+the same step as one paged_decode_append launch.
 
 "Write Triton Kv Cache Append Kernel", Failure modes and Performance requirements: under
 graph capture the batch is padded to a fixed size, padding tokens carry slot -1 and must be
 no-ops, and the launch grid may depend only on shapes.  Here the step is captured once at
 batch 16 and replayed with 16, 11 and 3 live requests (the rest padded: slot -1, context
-length 0, so their output rows must be 0), with new data copied into the captured buffers
-between replays.  Every replay is checked against an eager run of the same calls (pools bit
+length 0, so their output rows must be 0; the fused launch appends nothing for them), with new
+data copied into the captured buffers between replays.  Every replay is checked against an eager run of the same calls (pools bit
 for bit, outputs within the attention tolerance, since the decode's summation order depends
 on timing) and against the float64 oracle.
 """
@@ -34,7 +35,8 @@ def _scenario(data_seed, live):
     return wl, slots, ctx
 
 
-def test_graph_step_padded_batch():
+@pytest.mark.parametrize("fused", [False, True], ids=["two-calls", "fused"])
+def test_graph_step_padded_batch(fused):
     P = need_gpu()
     wl0, _, _ = _scenario(1, BMAX)
     maxctx = int(wl0.block_tables.shape[1]) * wl0.block_size
@@ -44,6 +46,10 @@ def test_graph_step_padded_batch():
     ws = P.decode_workspace(BMAX, wl0.num_q_heads, wl0.num_kv_heads, wl0.head_dim, maxctx)
 
     def step(d, out, workspace):
+        if fused:           # the new token of request b at position ctx[b] - 1, slot from its table
+            P.paged_decode_append(d["q"], d["nk"], d["nv"], d["k"], d["v"], d["bt"], d["ctx"], maxctx,
+                                  wl0.sm_scale, workspace=workspace, out=out)
+            return
         P.kv_append(d["nk"], d["nv"], d["slots"], d["k"], d["v"])
         P.paged_decode(d["q"], d["k"], d["v"], d["bt"], d["ctx"], maxctx, wl0.sm_scale,
                        workspace=workspace, out=out)
@@ -62,7 +68,8 @@ def test_graph_step_padded_batch():
     dn = dtype_name(wl0.dtype)
     for data_seed, live in ((11, BMAX), (12, 11), (13, 3), (14, BMAX)):
         wl, slots, ctx = _scenario(data_seed, live)
-        print(f"replay: data_seed {data_seed}, {live} live requests of {BMAX}", flush=True)
+        print(f"replay ({'fused' if fused else 'two calls'}): data_seed {data_seed}, {live} live requests "
+              f"of {BMAX}", flush=True)
         for key, src in (("q", wl.q), ("k", wl.k_pool), ("v", wl.v_pool), ("nk", wl.new_k),
                          ("nv", wl.new_v), ("slots", slots), ("ctx", ctx)):
             dev[key].copy_(src)
