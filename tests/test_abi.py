@@ -166,6 +166,27 @@ def test_decode_scaled_validation(lib, kw, status):
     assert _decode_scaled(lib, **kw) == status
 
 
+def _decode_append(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, qdt=1, qsb=4096, qsh=128, osb=4096, osh=128, kn=FAKE, vn=FAKE,
+             knb=1024, knh=128, vnb=1024, vnh=128, kc=FAKE, vc=FAKE, cdt=1, cb=16384, cs=1024, ch=128,
+             km=None, vm=None, bt=FAKE, bts=257, ctx=FAKE, B=64, Hq=32, Hkv=8, D=128, bs=16, nb=1000,
+             maxctx=4097, scale=0.088, ps=0, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.paged_decode_append(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kn=None), -1), (dict(vn=None), -1),
+    (dict(kn=FAKE8), -1), (dict(vn=FAKE + 2), -1),         # new rows must be 16-byte aligned
+    (dict(knb=1020), -1), (dict(vnh=-128), -1),            # ... and so must their strides
+    (dict(out=None), -1), (dict(cdt=2), -1),               # the decode's own checks still apply
+    (dict(Hq=24, Hkv=8), -2), (dict(ws=None), -3), (dict(scale=float("nan")), -1),
+    (dict(B=0), 0),                                        # nothing to append or decode
+])
+def test_decode_append_validation(lib, kw, status):
+    assert _decode_append(lib, **kw) == status
+
+
 def _slots(lib, **kw):
     a = dict(req=FAKE, pos=FAKE, T=16, bt=FAKE, bts=8, B=4, bs=16, out=FAKE, stream=None)
     a.update(kw)
