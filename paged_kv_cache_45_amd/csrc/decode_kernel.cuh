@@ -713,6 +713,58 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
       }
     }
   }
+  if constexpr (KIND == CacheKind::U3 && OWN && G <= kMfmaMaxG && NI == 4) {
+    // 3-bit V on the matrix cores at 16 bits: per element e of the lane's 8, one
+    // v_mfma_f32_4x4x4f16 sums the chunk's 4 tokens (k = token i).  A: lane q of a quad gives
+    // its own head's weights w_i = p_i s_i (fp16, round to nearest even: p <= 1 and s is an fp16
+    // value, so w cannot overflow); B: lane n gives element e of the 4 tokens as the exact fp16
+    // value 8 + code (bits 0x4800 | code << 7).  Register m of lane n then gains
+    // sum_i w_i (8 + code_i) for head m, as the fp32 form's sum_i (p_i s_i) code_i plus
+    // 8 sum_i w_i.  The zero-point sum takes the same rounded weights, sum_i w_i (z_i + 8), so
+    // that acc - zc = sum_i w_i (code_i - z_i) as before.  The 8 (not 1024 + code, whose fp16
+    // bits need no shift) keeps the offset within 3 bits of the codes in the fp32 sums.
+    const uint32_t sel = (uint32_t)((3 * c) & 3) * 0x01010101u + 0x02010100u;
+    uint32_t u[NI][4];                 // token i: (8 + code e, 8 + code e + 4) as fp16, e = 0..3
+    uint32_t wp[2];                    // the weights of tokens (0, 1) and (2, 3), fp16 pairs
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      // y = [octet bits 0..15 | octet bits 8..23]: code e at bit 3e of the low half, code e + 4
+      // at bit 3e + 4 of the high half; each is moved to bits 7..9 of its half
+      const u16x2_t y = __builtin_bit_cast(u16x2_t, __builtin_amdgcn_perm(R.vhi[i], R.vlo[i], sel));
+      const u16x2_t s0 = {7, 3}, s1 = {4, 0}, s2a = {0, 3}, s2b = {1, 0}, s3 = {2, 6};
+      u[i][0] = (__builtin_bit_cast(uint32_t, (u16x2_t)(y << s0)) & 0x03800380u) | 0x48004800u;
+      u[i][1] = (__builtin_bit_cast(uint32_t, (u16x2_t)(y << s1)) & 0x03800380u) | 0x48004800u;
+      u[i][2] = (__builtin_bit_cast(uint32_t, (u16x2_t)((u16x2_t)(y >> s2a) << s2b)) & 0x03800380u) | 0x48004800u;
+      u[i][3] = (__builtin_bit_cast(uint32_t, (u16x2_t)(y >> s3)) & 0x03800380u) | 0x48004800u;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      _Float16 wh[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int i = 2 * j + t;
+        const float vs = valid[i] ? f16_lo(vmt[i]) : 0.f;
+        const float vz = valid[i] ? f16_hi(vmt[i]) : 0.f;
+        wh[t] = (_Float16)(ppo[i][0] * vs);
+        S.zco[0] = fmaf((float)wh[t], vz + 8.f, S.zco[0]);
+      }
+      // heads q >= G of a 2-head group add nothing (their columns repeat heads 0 and 1)
+      wp[j] = (G == 4 || q < G) ? (uint32_t)__builtin_bit_cast(uint16_t, wh[0]) |
+                                      ((uint32_t)__builtin_bit_cast(uint16_t, wh[1]) << 16)
+                                : 0u;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // element e: the low halves of the 4 tokens; element e + 4: the high halves
+      const uint32_t lo01 = __builtin_amdgcn_perm(u[1][e], u[0][e], 0x05040100u);
+      const uint32_t lo23 = __builtin_amdgcn_perm(u[3][e], u[2][e], 0x05040100u);
+      const uint32_t hi01 = __builtin_amdgcn_perm(u[1][e], u[0][e], 0x07060302u);
+      const uint32_t hi23 = __builtin_amdgcn_perm(u[3][e], u[2][e], 0x07060302u);
+      S.acc4[0][e] = mfma4x4x4<false>(wp[0], wp[1], lo01, lo23, S.acc4[0][e]);
+      S.acc4[0][e + 4] = mfma4x4x4<false>(wp[0], wp[1], hi01, hi23, S.acc4[0][e + 4]);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     float vf[8];
