@@ -82,12 +82,12 @@ constexpr int kClaimUnitChunks = 0;
 // a workgroup that starts a segment inside its range first waits for the segment's context
 // length, q and block table: charged to the static split as this many tokens of work
 // (measured with one 8-wave workgroup per CU: 16 -> 48 gains 1 % on the Llama-8B step, 2 % on
-// the 3-bit decode; 32 and 48 are equal on the former).  A byte-code token costs about half a
-// 16-bit one, so the same wait is worth more of them: 96 measured best for fp8, e5m2 and int8
-// at the Llama-8B shape (+0.6-0.9 %, +1.0 %, +1.8-2.5 % against 48; 24, 144 and 192 slower);
-// the 3-bit decode is the same with 48 or 96.
+// the 3-bit decode; 32 and 48 are equal on the former).  A coded-cache token costs about half a
+// 16-bit one or less, so the same wait is worth more of them: 96 measured best for fp8, e5m2
+// and int8 at the Llama-8B shape (+0.6-0.9 %, +1.0 %, +1.8-2.5 % against 48; 24, 144 and 192
+// slower) and for the 3-bit decode with its 16-bit PV products (+0.9 %).
 constexpr int kSegmentStartTokens = 48;
-constexpr int kSegmentStartTokensByte = 96;
+constexpr int kSegmentStartTokensCoded = 96;
 // block hand-out counters per (request, kv-head group) segment: one per head wave
 constexpr size_t kClaimCounters = 4;
 
@@ -405,7 +405,8 @@ static int decode_impl(void* out, const void* q, pkv_dtype q_dtype,
   p.partition_size = ps;
   p.num_wgs = L.plan.num_wgs;
   p.split_tier = L.plan.split_tier;
-  p.seg_start_units = ((is_byte_code(cache_dtype) ? kSegmentStartTokensByte : kSegmentStartTokens) + ps / 2) / ps;
+  p.seg_start_units =
+      ((is_byte_code(cache_dtype) || cache_dtype == PKV_U3 ? kSegmentStartTokensCoded : kSegmentStartTokens) + ps / 2) / ps;
   p.heads_per_group = L.plan.heads_per_group;
   p.num_head_groups = L.plan.num_head_groups;
   p.token_streams = L.plan.token_streams;
