@@ -411,6 +411,8 @@ static int decode_impl(void* out, const void* q, pkv_dtype q_dtype,
   p.num_head_groups = L.plan.num_head_groups;
   p.token_streams = L.plan.token_streams;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
+  p.u3_code_mask = 0x03800380u;
+  p.u3_code_bias = 0x48004800u;
   char* ws = static_cast<char*>(workspace);
   p.ws_acc = reinterpret_cast<float*>(ws + L.acc_off);
   p.ws_ml = reinterpret_cast<float*>(ws + L.ml_off);

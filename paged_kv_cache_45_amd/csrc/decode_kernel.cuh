@@ -724,19 +724,40 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
     // that acc - zc = sum_i w_i (code_i - z_i) as before.  The 8 (not 1024 + code, whose fp16
     // bits need no shift) keeps the offset within 3 bits of the codes in the fp32 sums.
     const uint32_t sel = (uint32_t)((3 * c) & 3) * 0x01010101u + 0x02010100u;
-    uint32_t u[NI][4];                 // token i: (8 + code e, 8 + code e + 4) as fp16, e = 0..3
-    uint32_t wp[2];                    // the weights of tokens (0, 1) and (2, 3), fp16 pairs
+    // Token pair j = (2j, 2j + 1): each token's octet lined up by one byte permute
+    // (y = [octet bits 0..15 | octet bits 8..23]), then the two tokens' low halves and high
+    // halves paired by one more permute each: L = [bits 0..15 of token 2j | of token 2j + 1],
+    // H = [bits 8..23 of token 2j | of token 2j + 1].  Code e sits at bit 3e of each half of L and
+    // code e + 4 at bit 3e + 4 of each half of H, so one 32-bit shift moves both tokens' code to
+    // bits 7..9 of their halves (what a shift carries across the halves lands outside bits 7..9),
+    // and one mask-and-bias instruction gives the fp16 pair (8 + code of token 2j, of token
+    // 2j + 1): the B operand of element e (L) or e + 4 (H).
+    uint32_t bl[2][4], bh[2][4];
+    const uint32_t cmask = p.u3_code_mask;
+    // the bias in a vector register: v_and_or_b32 reads at most one scalar operand here
+    uint32_t vbias = p.u3_code_bias;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(vbias) : "s"(vbias));
+    auto mask_bias = [&](uint32_t x) {
+      uint32_t r;
+      asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(cmask), "v"(vbias));
+      return r;
+    };
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      // y = [octet bits 0..15 | octet bits 8..23]: code e at bit 3e of the low half, code e + 4
-      // at bit 3e + 4 of the high half; each is moved to bits 7..9 of its half
-      const u16x2_t y = __builtin_bit_cast(u16x2_t, __builtin_amdgcn_perm(R.vhi[i], R.vlo[i], sel));
-      const u16x2_t s0 = {7, 3}, s1 = {4, 0}, s2a = {0, 3}, s2b = {1, 0}, s3 = {2, 6};
-      u[i][0] = (__builtin_bit_cast(uint32_t, (u16x2_t)(y << s0)) & 0x03800380u) | 0x48004800u;
-      u[i][1] = (__builtin_bit_cast(uint32_t, (u16x2_t)(y << s1)) & 0x03800380u) | 0x48004800u;
-      u[i][2] = (__builtin_bit_cast(uint32_t, (u16x2_t)((u16x2_t)(y >> s2a) << s2b)) & 0x03800380u) | 0x48004800u;
-      u[i][3] = (__builtin_bit_cast(uint32_t, (u16x2_t)(y >> s3)) & 0x03800380u) | 0x48004800u;
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t y0 = __builtin_amdgcn_perm(R.vhi[2 * j], R.vlo[2 * j], sel);
+      const uint32_t y1 = __builtin_amdgcn_perm(R.vhi[2 * j + 1], R.vlo[2 * j + 1], sel);
+      const uint32_t L = __builtin_amdgcn_perm(y1, y0, 0x05040100u);
+      const uint32_t H = __builtin_amdgcn_perm(y1, y0, 0x07060302u);
+      bl[j][0] = mask_bias(L << 7);
+      bl[j][1] = mask_bias(L << 4);
+      bl[j][2] = mask_bias(L << 1);
+      bl[j][3] = mask_bias(L >> 2);
+      bh[j][0] = mask_bias(H << 3);
+      bh[j][1] = mask_bias(H);
+      bh[j][2] = mask_bias(H >> 3);
+      bh[j][3] = mask_bias(H >> 6);
     }
+    uint32_t wp[2];                    // the weights of tokens (0, 1) and (2, 3), fp16 pairs
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       _Float16 wh[2];
@@ -755,13 +776,8 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      // element e: the low halves of the 4 tokens; element e + 4: the high halves
-      const uint32_t lo01 = __builtin_amdgcn_perm(u[1][e], u[0][e], 0x05040100u);
-      const uint32_t lo23 = __builtin_amdgcn_perm(u[3][e], u[2][e], 0x05040100u);
-      const uint32_t hi01 = __builtin_amdgcn_perm(u[1][e], u[0][e], 0x07060302u);
-      const uint32_t hi23 = __builtin_amdgcn_perm(u[3][e], u[2][e], 0x07060302u);
-      S.acc4[0][e] = mfma4x4x4<false>(wp[0], wp[1], lo01, lo23, S.acc4[0][e]);
-      S.acc4[0][e + 4] = mfma4x4x4<false>(wp[0], wp[1], hi01, hi23, S.acc4[0][e + 4]);
+      S.acc4[0][e] = mfma4x4x4<false>(wp[0], wp[1], bl[0][e], bl[1][e], S.acc4[0][e]);
+      S.acc4[0][e + 4] = mfma4x4x4<false>(wp[0], wp[1], bh[0][e], bh[1][e], S.acc4[0][e + 4]);
     }
     return;
   }

@@ -58,6 +58,10 @@ struct DecodeParams {
   int num_head_groups;                // num_kv_heads / heads_per_group
   int token_streams;                  // waves sets of a workgroup splitting its chunks
   float scale_log2;                   // sm_scale * log2(e)
+  // 3-bit PV operands: the mask of bits 7..9 of each 16-bit half and the fp16 8.0 pair.  Passed
+  // in rather than written as literals, so that the compiler can fuse the mask and the bias into
+  // one three-operand instruction (whose encoding here takes no literal)
+  uint32_t u3_code_mask, u3_code_bias;
   float* ws_acc;                      // [num_wgs, 2, heads_per_group, G, D] partial accumulators
   float* ws_ml;                       // [num_wgs, 2, heads_per_group, G, 2] partial (m, l)
   int* ws_seg;                        // [batch, head groups, 2] first partial slot, last owner
