@@ -714,14 +714,14 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
     }
   }
   if constexpr (KIND == CacheKind::U3 && OWN && G <= kMfmaMaxG && NI == 4) {
-    // 3-bit V on the matrix cores at 16 bits: per element e of the lane's 8, one
-    // v_mfma_f32_4x4x4f16 sums the chunk's 4 tokens (k = token i).  A: lane q of a quad gives
-    // its own head's weights w_i = p_i s_i (fp16, round to nearest even: p <= 1 and s is an fp16
+    // 3-bit V on the matrix cores at 16 bits: per element e of the lane's 8, v_mfma_f32_4x4x4f16
+    // sums the chunk's 4 tokens (k = token i).  A: lane q of a quad gives its own head's weights
+    // w_i = p_i s_i, as two fp16 parts with one product each (below; p <= 1 and s is an fp16
     // value, so w cannot overflow); B: lane n gives element e of the 4 tokens as the exact fp16
     // value 8 + code (bits 0x4800 | code << 7).  Register m of lane n then gains
     // sum_i w_i (8 + code_i) for head m, as the fp32 form's sum_i (p_i s_i) code_i plus
-    // 8 sum_i w_i.  The zero-point sum takes the same rounded weights, sum_i w_i (z_i + 8), so
-    // that acc - zc = sum_i w_i (code_i - z_i) as before.  The 8 (not 1024 + code, whose fp16
+    // 8 sum_i w_i.  The zero-point sum takes the same weights, sum_i w_i (z_i + 8), so that
+    // acc - zc = sum_i w_i (code_i - z_i) as before.  The 8 (not 1024 + code, whose fp16
     // bits need no shift) keeps the offset within 3 bits of the codes in the fp32 sums.
     const uint32_t sel = (uint32_t)((3 * c) & 3) * 0x01010101u + 0x02010100u;
     // Token pair j = (2j, 2j + 1): each token's octet lined up by one byte permute
@@ -757,27 +757,38 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
       bh[j][2] = mask_bias(H >> 3);
       bh[j][3] = mask_bias(H >> 6);
     }
-    uint32_t wp[2];                    // the weights of tokens (0, 1) and (2, 3), fp16 pairs
+    // the weights of tokens (0, 1) and (2, 3) as fp16 pairs, each weight w split into its fp16
+    // rounding and the fp16 rounding of the rest (w - hi is exact in fp32), so that the two
+    // products together carry w to about 2^-24 relative, like the fp32 form: with a single fp16
+    // weight an output that is a small difference of large values (V rows of both signs with a
+    // large scale) could lose more than the decode's tolerance
+    uint32_t wp[2], wq[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      _Float16 wh[2];
+      _Float16 wh[2], wl[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int i = 2 * j + t;
         const float vs = valid[i] ? f16_lo(vmt[i]) : 0.f;
         const float vz = valid[i] ? f16_hi(vmt[i]) : 0.f;
-        wh[t] = (_Float16)(ppo[i][0] * vs);
-        S.zco[0] = fmaf((float)wh[t], vz + 8.f, S.zco[0]);
+        const float w = ppo[i][0] * vs;
+        wh[t] = (_Float16)w;
+        wl[t] = (_Float16)(w - (float)wh[t]);
+        S.zco[0] = fmaf(w, vz + 8.f, S.zco[0]);
       }
       // heads q >= G of a 2-head group add nothing (their columns repeat heads 0 and 1)
-      wp[j] = (G == 4 || q < G) ? (uint32_t)__builtin_bit_cast(uint16_t, wh[0]) |
-                                      ((uint32_t)__builtin_bit_cast(uint16_t, wh[1]) << 16)
-                                : 0u;
+      const bool live = G == 4 || q < G;
+      wp[j] = live ? (uint32_t)__builtin_bit_cast(uint16_t, wh[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, wh[1]) << 16)
+                   : 0u;
+      wq[j] = live ? (uint32_t)__builtin_bit_cast(uint16_t, wl[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, wl[1]) << 16)
+                   : 0u;
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       S.acc4[0][e] = mfma4x4x4<false>(wp[0], wp[1], bl[0][e], bl[1][e], S.acc4[0][e]);
       S.acc4[0][e + 4] = mfma4x4x4<false>(wp[0], wp[1], bh[0][e], bh[1][e], S.acc4[0][e + 4]);
+      S.acc4[0][e] = mfma4x4x4<false>(wq[0], wq[1], bl[0][e], bl[1][e], S.acc4[0][e]);
+      S.acc4[0][e + 4] = mfma4x4x4<false>(wq[0], wq[1], bh[0][e], bh[1][e], S.acc4[0][e + 4]);
     }
     return;
   }

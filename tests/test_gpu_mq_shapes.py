@@ -97,3 +97,35 @@ def test_matrix_core_form_shapes(kind, G, D, bs, dtype):
         got = f32_of(out)
         assert np.all(got[LENS.index(0)] == 0)
         assert report(f"mq {kind} G{G} D{D} bs{bs} {dtype_name(dtype)} ps{ps}", got, want, dtype) <= ATTN_TOL
+
+
+@pytest.mark.parametrize("G,D", [(4, 128), (2, 64)])
+def test_u3_large_cancelling_values(G, D):
+    """3-bit V rows of magnitude ~500 whose signs alternate from token to token; tokens 2i and
+    2i + 1 share one key, so each pair gets the same probability and cancels but for its small
+    noise: every output is a small difference of large values.  The row scales differ within a
+    pair, so rounding the weights p s of the PV products to a single fp16 each would leave
+    ~2^-12 x 500 of each pair (the matrix-core PV form carries each weight as two fp16 parts).  Against the oracle at the
+    decode's tolerance.  Pages: "triton-3bit-kv-cache-kernel" README, section 2 test 3 (the
+    affine dequantisation); "Triton KV Cache and PagedAttention", reference answer TODO 3-5."""
+    P = need_gpu()
+    Hkv, bs = 8, 16
+    lens = [2, 4, 16, 64, 256, 700]             # even: the alternating signs cancel exactly
+    wl = W.decode_workload("u3-cancel", batch=len(lens), num_q_heads=G * Hkv, num_kv_heads=Hkv,
+                           head_dim=D, block_size=bs, ctx_lo=0, ctx_hi=0, dtype=torch.float16,
+                           device="cuda", seed=811 + G + D, append_one=False, ctx_override=lens,
+                           poison=False)
+    NB = wl.k_pool.shape[0]
+    gen = torch.Generator(device="cpu").manual_seed(812 + G + D)
+    sign = torch.where(torch.arange(bs) % 2 == 0, 1.0, -1.0).view(1, bs, 1, 1)
+    v = 500.0 * sign + 20.0 * (2 * torch.rand((NB, bs, Hkv, D), generator=gen) - 1)
+    wl.v_pool.copy_(v.to(torch.float16))
+    wl.k_pool[:, 1::2].copy_(wl.k_pool[:, 0::2])       # one key per token pair
+    (kc, vc, km, vm), (kpool, vpool) = _pools(P, wl, "u3", _live(wl, lens))
+    want = paged_decode_ref(f32_of(wl.q), kpool, vpool, wl.block_tables.numpy(), np.array(lens), bs,
+                            Hkv, wl.sm_scale)
+    assert np.abs(want).max() < 30.0          # the outputs do cancel
+    for ps in (0, 512):
+        out = P.paged_decode(wl.q, kc, vc, wl.block_tables.cuda(), wl.ctx_after.cuda(), max(lens),
+                             wl.sm_scale, k_meta=km, v_meta=vm, partition_size=ps, cache_dtype="u3")
+        assert report(f"u3 cancelling G{G} D{D} ps{ps}", f32_of(out), want, torch.float16) <= ATTN_TOL
