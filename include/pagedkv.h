@@ -175,9 +175,7 @@ size_t paged_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads,
  * context_lens[b] tokens, token t read from physical block block_tables[b, t /
  * block_size] at slot t % block_size; GQA per [Append] (query head h reads kv head
  * h / (num_q_heads / num_kv_heads)); with the 3-bit cache the codes are unpacked and
- * dequantised, x = (q - z) * s, on the fly ([3bit], title paragraph, section 2 test 3;
- * with up to 4 query heads per kv head the weights p * s of the probability-weighted sum are
- * rounded to fp16, a relative 2^-12, inside the decode's 2e-3 tolerance);
+ * dequantised, x = (q - z) * s, on the fly ([3bit], title paragraph, section 2 test 3);
  * with a byte-code cache (fp8 e4m3fn, fp8 e5m2, int8) each row reads as decode(code) * s,
  * the inverse of the kv_append quantiser ([Append], Inputs item 4 and Correctness
  * requirements: the quantised cache is read back through the row's scale), with s applied to
