@@ -156,10 +156,8 @@ int kv_append_scaled(const void* k_new, const void* v_new, pkv_dtype in_dtype,
  * reduced independently and merged by log-sum-exp.  The library balances the work by
  * giving each resident workgroup of the current device a share of all (request, kv head,
  * granule) units sized to its expected speed, where a granule is `partition_size` tokens;
- * a context is cut at multiples of the granule, except that where a block of the cache
- * holds at least 64 KB of a wave's K/V the workgroups sharing a context hand its blocks out
- * among themselves at run time, a block at a time.  The workspace holds the partial states of the ranges that get
- * cut, so its size depends on the current device's compute-unit count: query it on the
+ * a context is cut at multiples of the granule.  The workspace holds the partial states of
+ * the ranges that get cut, so its size depends on the current device's compute-unit count: query it on the
  * device that will run the call.
  * partition_size: 0 = automatic (16 tokens, the finest balance), else a multiple of 16.
  * Returns 0 for batch 0 and (size_t)-1 for invalid arguments (batch above 8192 included).
@@ -199,18 +197,15 @@ size_t paged_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads,
  *                    paged_decode_workspace_size.
  *   workspace        device, >= paged_decode_workspace_size(...) bytes, 256-byte aligned,
  *                    with any contents: a call reads nothing from it that the same call did
- *                    not write first (the counters through which the workgroups sharing a
- *                    (request, head group) hand out its blocks at run time are cleared by a
- *                    kernel of the call, ahead of the decode), so a fresh uninitialised
- *                    allocation is fine and one workspace serves calls of every shape it is
+ *                    not write first, so a fresh uninitialised allocation is fine and one workspace serves calls of every shape it is
  *                    large enough for.  Calls sharing a workspace must be ordered (same
  *                    stream, or synchronised); overlapping calls on it race.
  *   batch            0 .. 8192.
  * Accumulation is fp32; outputs are rounded to q_dtype to nearest even.
  * Reproducibility: results are fixed up to the order of the fp32 additions.  The token streams
- * of a workgroup share a range's chunks at run time, and the workgroups that share a long
- * segment share its blocks, so which wave sums which tokens, and in which order, depends on
- * timing.  Two calls on the same inputs attend over the same tokens with the same weights and
+ * of a workgroup share a range's chunks at run time, so which wave sums which tokens, and in
+ * which order, depends on timing (which workgroup reads which tokens does not: the split over
+ * workgroups is fixed by the context lengths and the partition size).  Two calls on the same inputs attend over the same tokens with the same weights and
  * agree to within fp32 rounding of the sums (far inside the 2e-3 attention tolerance), not bit
  * for bit.
  */
@@ -268,9 +263,7 @@ int paged_decode_scaled(void* out, const void* q, pkv_dtype q_dtype,
  *                    computes them) and for paged_decode (read).
  *   other arguments  as for paged_decode.  The context lengths count the new token.
  * A block id outside [0, num_blocks) skips that request's write, as kv_append skips a slot
- * outside the pool.  Long segments are not handed out at run time in this call (every segment's
- * last token must have one reader), so the split is static.  The workspace is shared with
- * paged_decode (same size query).
+ * outside the pool.  The workspace is shared with paged_decode (same size query).
  */
 int paged_decode_append(void* out, const void* q, pkv_dtype q_dtype,
                         int64_t q_stride_b, int64_t q_stride_h, int64_t o_stride_b, int64_t o_stride_h,

@@ -67,18 +67,11 @@ constexpr int kMaxBatch = 8192;       // the decode kernel keeps batch + 1 prefi
 //    Llama-8B step 0.602 -> 0.607 of HBM peak;
 //  * static split, 3-bit cache (VALU-bound, so the XCDs' memory paths do not matter): first
 //    tier 96 helps (+0.4 %), the odd-XCD weight costs 1 %;
-//  * run-time block hand-out (long context): 88 / 64; 96 costs 3 %.
+//  * long-context decode (64-token blocks, 32k-128k contexts): 88 / 64 and 96 / 92 / 64 / 61
+//    equal within noise.
 struct SplitWeights { int64_t first_even, first_odd, rest_even, rest_odd; };
 constexpr SplitWeights kSplitStatic{96, 92, 64, 61};
 constexpr SplitWeights kSplitStaticU3{96, 96, 64, 64};
-constexpr SplitWeights kSplitClaimed{88, 88, 64, 64};
-// run-time hand-out of shared segments: from this many bytes of K/V per wave and block, in
-// units of this many chunks (0: whole blocks).  Measured on the long-context decode (64-token
-// blocks, 4-token chunks): with the own-head decode form whole blocks are 2.5 % faster than
-// 8-chunk units (with the replicated form 8-chunk units had been 1 % faster); 4-chunk units are
-// 30 % slower: each claim is a device-scope atomic on a counter that every sharer uses.
-constexpr int64_t kClaimMinBlockBytes = 64 * 1024;
-constexpr int kClaimUnitChunks = 0;
 // a workgroup that starts a segment inside its range first waits for the segment's context
 // length, q and block table: charged to the static split as this many tokens of work
 // (measured with one 8-wave workgroup per CU: 16 -> 48 gains 1 % on the Llama-8B step, 2 % on
@@ -88,19 +81,16 @@ constexpr int kClaimUnitChunks = 0;
 // slower) and for the 3-bit decode with its 16-bit PV products (+0.9 %).
 constexpr int kSegmentStartTokens = 48;
 constexpr int kSegmentStartTokensCoded = 96;
-// block hand-out counters per (request, kv-head group) segment: one per head wave
-constexpr size_t kClaimCounters = 4;
 
 struct DecodeLayout {
   pkv::DecodePlan plan;
-  size_t claim_off, acc_off, ml_off, seg_off, bytes;
+  size_t acc_off, ml_off, seg_off, bytes;
 };
 
-// Workspace layout of paged_decode: the block hand-out counters (kClaimCounters per segment), the
-// partial accumulators, the partial (m, l), and per segment (request, kv-head group) the slot of
-// its first partial and the owner of its last unit.  Every call writes each part before it reads
-// it (the counters through the clearing kernel ahead of the decode), so the workspace needs no
-// particular contents and one workspace serves calls of every shape it is large enough for.
+// Workspace layout of paged_decode: the partial accumulators, the partial (m, l), and per
+// segment (request, kv-head group) the slot of its first partial and the owner of its last unit.
+// Every call writes each part before it reads it, so the workspace needs no particular contents
+// and one workspace serves calls of every shape it is large enough for.
 DecodeLayout decode_layout(int batch, int num_q_heads, int num_kv_heads, int head_dim,
                            int max_context_len, int ps, int bf16, int kind) {
   DecodeLayout L{};
@@ -108,9 +98,7 @@ DecodeLayout decode_layout(int batch, int num_q_heads, int num_kv_heads, int hea
   L.plan = pkv::plan_decode(batch, num_q_heads, num_kv_heads, head_dim, max_context_len, ps, bf16, kind);
   const size_t slots = (size_t)L.plan.num_wgs * 2 * L.plan.heads_per_group * group;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const size_t segs = (size_t)batch * L.plan.num_head_groups;
-  L.claim_off = 0;
-  L.acc_off = up(segs * kClaimCounters * sizeof(int));
+  L.acc_off = 0;
   L.ml_off = L.acc_off + up(slots * head_dim * sizeof(float));
   L.seg_off = L.ml_off + up(slots * 2 * sizeof(float));
   L.bytes = L.seg_off + up((size_t)batch * L.plan.num_head_groups * 2 * sizeof(int));
@@ -417,28 +405,7 @@ static int decode_impl(void* out, const void* q, pkv_dtype q_dtype,
   p.ws_acc = reinterpret_cast<float*>(ws + L.acc_off);
   p.ws_ml = reinterpret_cast<float*>(ws + L.ml_off);
   p.ws_seg = reinterpret_cast<int*>(ws + L.seg_off);
-  p.ws_claim = reinterpret_cast<int*>(ws + L.claim_off);
-  // Block claiming: a wave takes whole claim units (kClaimUnitChunks chunks inside one block,
-  // or whole blocks), and its share of the bandwidth is small (~1/2000 of the device), so a
-  // claim of B bytes keeps it busy for ~B / 3 GB/s, and every claim is a device-scope atomic.
-  // It pays only where blocks are large enough for the claims to outweigh their cost and
-  // coarse enough split granules leave a tail (measured: 128 KB blocks of the long-context
-  // decode gain ~10 %, 32 KB blocks of the Llama-8B step lose 15 %): at least 64 KB of K/V per
-  // wave and block.  It also needs an even number of chunks per unit and at most 4 head waves.
-  const int64_t row_bytes = cache_dtype == PKV_U3    ? 2 * (head_dim * 3 / 8 + 4)
-                            : is_byte_code(cache_dtype) ? 2 * (int64_t)(head_dim + 4)
-                                                            : 4 * (int64_t)head_dim;
-  const int64_t wave_block_bytes = (int64_t)block_size * L.plan.hpi * row_bytes;
-  const int unit_tokens = kClaimUnitChunks > 0 ? std::min(block_size, kClaimUnitChunks * L.plan.chunk_tokens)
-                                               : block_size;
-  p.claim_units = (wave_block_bytes >= kClaimMinBlockBytes && unit_tokens % (L.plan.chunk_tokens * 2) == 0 &&
-                   L.plan.heads_per_group / L.plan.hpi <= kClaimCounters) ? 1 : 0;
-  p.log2_claim = 0;
-  while ((1 << p.log2_claim) < unit_tokens) ++p.log2_claim;
   if (nr) {
-    // the fused append needs the one reader of each request's last token to be the workgroup
-    // holding its last granule: no run-time hand-out, whose units any sharer may take
-    p.claim_units = 0;
     p.k_new = nr->k;
     p.v_new = nr->v;
     p.kn_sb = nr->k_sb;
@@ -446,7 +413,7 @@ static int decode_impl(void* out, const void* q, pkv_dtype q_dtype,
     p.vn_sb = nr->v_sb;
     p.vn_sh = nr->v_sh;
   }
-  const SplitWeights sw = p.claim_units ? kSplitClaimed : cache_dtype == PKV_U3 ? kSplitStaticU3 : kSplitStatic;
+  const SplitWeights sw = cache_dtype == PKV_U3 ? kSplitStaticU3 : kSplitStatic;
   p.split_w[0] = sw.first_even;
   p.split_w[1] = sw.first_odd;
   p.split_w[2] = sw.rest_even;

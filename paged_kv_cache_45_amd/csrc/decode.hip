@@ -86,16 +86,6 @@ __global__ __launch_bounds__(D * kMergeMaxSplit) void merge_kernel(DecodeParams 
   }
 }
 
-// The run-time block hand-out counts the claims of each shared (request, head group) segment
-// from zero.  Its counters (kClaimWaves per segment, at the head of the workspace) are cleared by
-// this kernel ahead of the decode kernel of the same call, so a call reads nothing from the
-// workspace that it did not write itself: any earlier contents (a fresh allocation, another
-// shape's partials, a call whose later launch failed) give the same result.  A kernel, not a
-// memset, so that a captured call records no memset node.
-__global__ __launch_bounds__(256) void claim_clear_kernel(int* counters, int n) {
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) counters[i] = 0;
-}
-
 // ---------------------------------------------------------------------------------------
 // Host side: geometry, occupancy-sized grid, dispatch.
 // ---------------------------------------------------------------------------------------
@@ -108,19 +98,19 @@ int heads_per_instr(int head_dim, int num_kv_heads) {
   return hpi;
 }
 
-const void* decode_kernel_ptr(int head_dim, int group, bool bf16, CacheKind kind, int hpi, bool claim) {
+const void* decode_kernel_ptr(int head_dim, int group, bool bf16, CacheKind kind, int hpi) {
   const bool d128 = head_dim == 128;
   switch (kind) {
     case CacheKind::U3:
-      return d128 ? decode_kernel_ptr_u3_d128(group, bf16, hpi, claim) : decode_kernel_ptr_u3_d64(group, bf16, hpi, claim);
+      return d128 ? decode_kernel_ptr_u3_d128(group, bf16, hpi) : decode_kernel_ptr_u3_d64(group, bf16, hpi);
     case CacheKind::Fp8:
-      return d128 ? decode_kernel_ptr_fp8_d128(group, bf16, hpi, claim) : decode_kernel_ptr_fp8_d64(group, bf16, hpi, claim);
+      return d128 ? decode_kernel_ptr_fp8_d128(group, bf16, hpi) : decode_kernel_ptr_fp8_d64(group, bf16, hpi);
     case CacheKind::E5m2:
-      return d128 ? decode_kernel_ptr_e5m2_d128(group, bf16, hpi, claim) : decode_kernel_ptr_e5m2_d64(group, bf16, hpi, claim);
+      return d128 ? decode_kernel_ptr_e5m2_d128(group, bf16, hpi) : decode_kernel_ptr_e5m2_d64(group, bf16, hpi);
     case CacheKind::I8:
-      return d128 ? decode_kernel_ptr_i8_d128(group, bf16, hpi, claim) : decode_kernel_ptr_i8_d64(group, bf16, hpi, claim);
+      return d128 ? decode_kernel_ptr_i8_d128(group, bf16, hpi) : decode_kernel_ptr_i8_d64(group, bf16, hpi);
     default:
-      return d128 ? decode_kernel_ptr_same_d128(group, bf16, hpi, claim) : decode_kernel_ptr_same_d64(group, bf16, hpi, claim);
+      return d128 ? decode_kernel_ptr_same_d128(group, bf16, hpi) : decode_kernel_ptr_same_d64(group, bf16, hpi);
   }
 }
 
@@ -177,7 +167,7 @@ DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int head_di
     for (int kd = 0; kd < kNumCacheKinds; ++kd) {    // every CacheKind value
       if ((bf16 >= 0 && bf != bf16) || (kind >= 0 && kd != kind)) continue;
       const CacheKind ck = static_cast<CacheKind>(kd);
-      per_cu = std::max(per_cu, resident_wgs_per_cu(decode_kernel_ptr(head_dim, group, bf != 0, ck, P.hpi, false),
+      per_cu = std::max(per_cu, resident_wgs_per_cu(decode_kernel_ptr(head_dim, group, bf != 0, ck, P.hpi),
                                                     P.waves_per_wg * 64, P.lds_bytes));
     }
   const int64_t units = (int64_t)batch * P.num_head_groups *
@@ -191,20 +181,11 @@ DecodePlan plan_decode(int batch, int num_q_heads, int num_kv_heads, int head_di
 hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan, CacheKind kind, bool bf16,
                          int head_dim, int group, hipStream_t s) {
   if (p.batch == 0) return hipSuccess;
-  const void* fn = decode_kernel_ptr(head_dim, group, bf16, kind, plan.hpi, p.claim_units != 0);
+  const void* fn = decode_kernel_ptr(head_dim, group, bf16, kind, plan.hpi);
   const void* mf = merge_kernel_ptr(head_dim, group, bf16);
   if (!fn || !mf) return hipErrorInvalidValue;
   void* args[] = {const_cast<DecodeParams*>(&p)};
-  hipError_t e = hipSuccess;
-  if (p.claim_units) {
-    int* counters = p.ws_claim;
-    int n = (int)((int64_t)p.batch * plan.num_head_groups * kClaimWaves);
-    void* cargs[] = {&counters, &n};
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&claim_clear_kernel),
-                        dim3((unsigned)std::min(64, (n + 255) / 256)), dim3(256), cargs, 0, s);
-    if (e != hipSuccess) return e;
-  }
-  e = hipLaunchKernel(fn, dim3((unsigned)plan.num_wgs), dim3(plan.waves_per_wg * 64), args,
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)plan.num_wgs), dim3(plan.waves_per_wg * 64), args,
                       plan.lds_bytes, s);
   if (e != hipSuccess) return e;
   // split the partials of a segment so that each thread merges about 2 x kMergeBatch of them

@@ -3,8 +3,8 @@
 
 namespace pkv {
 
-const void* decode_kernel_ptr_e5m2_d64(int group, bool bf16, int hpi, bool claim) {
-  return kernel_by_dtype<64, CacheKind::E5m2>(group, bf16, hpi, claim);
+const void* decode_kernel_ptr_e5m2_d64(int group, bool bf16, int hpi) {
+  return kernel_by_dtype<64, CacheKind::E5m2>(group, bf16, hpi);
 }
 
 }  // namespace pkv

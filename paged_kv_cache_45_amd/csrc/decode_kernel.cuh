@@ -57,7 +57,6 @@ namespace pkv {
 #endif
 
 constexpr int kMaxWaves = 8;        // waves per workgroup at most (token streams x head group)
-constexpr int kClaimWaves = 4;      // block counters per segment (one per head wave)
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 
@@ -986,88 +985,6 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, State<G>& S, in
   }
 }
 
-// The full claim units [0, nu) of a segment shared by several workgroups (unit u = tokens
-// [u * UT, u * UT + UT), UT = 2^log2_ut tokens inside one block), handed out one unit at a time
-// to each wave from a counter of the segment in the workspace (one counter per head wave,
-// shared by that head wave's token streams in every sharing workgroup): whichever wave is ready
-// takes the next unit, so the sharers, which run on different XCDs at different speeds, finish
-// the segment together instead of each finishing a fixed share.  Per wave, with no barrier:
-// lane 0 claims one unit ahead of the one being read, the block id comes through the scalar
-// cache (so its wait never drains the vector loads), and the next unit's first chunk is issued
-// before the current unit's last chunk is computed.  A wave reads all chunks of each unit it
-// claims (an even count).
-template <int D, int G, bool BF16, CacheKind KIND, int HPI>
-__device__ __forceinline__ void run_claimed(const DecodeParams& p, State<G>& S, int b, int hg, int nu,
-                                            int* claim, int lane, int tr, int hh, int c) {
-  using Gm = Geo<D, HPI, G>;
-  using R = Regs<Gm::NI, KIND>;
-  constexpr int esz = KIND == CacheKind::U3 ? 4 : byte_kind(KIND) ? 1 : 2;
-  const int my_n = (1 << p.log2_claim) / Gm::CT;          // chunks per unit
-  typedef const __attribute__((address_space(4))) int32_t* ConstIntPtr;
-  const ConstIntPtr bt_row = (ConstIntPtr)(p.block_tables + b * p.bt_sb);
-  const int h_first = hg * p.heads_per_group;
-  const LaneOffsets<D, HPI, KIND, G> lo = lane_offsets<D, HPI, KIND, G>(p, tr, hh, c);
-  const char* kc = static_cast<const char*>(p.k_cache) + (int64_t)h_first * p.c_sh * esz;
-  const char* vc = static_cast<const char*>(p.v_cache) + (int64_t)h_first * p.c_sh * esz;
-  const char* kmc = static_cast<const char*>(p.k_meta) + (int64_t)h_first * p.m_sh * 4;
-  const char* vmc = static_cast<const char*>(p.v_meta) + (int64_t)h_first * p.m_sh * 4;
-  // the counters are cleared by a kernel ahead of this one in the same call; a claim outside
-  // [0, nu) ends the loop, so no claim can read outside the segment
-  auto take = [&](int v) { return (unsigned)v < (unsigned)nu ? v : nu; };
-  typedef __attribute__((address_space(1))) int GlobalInt;
-  GlobalInt* const claim_g = (GlobalInt*)claim;          // a global atomic (vmcnt only)
-  auto claim_async = [&]() {
-    int v = 0;
-    if (lane == 0) v = __hip_atomic_fetch_add(claim_g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return v;
-  };
-  // unit u's block (id through the scalar cache) and first slot in it
-  struct Loc { int64_t phys; int slot; };
-  auto loc_of = [&](int u) {
-    Loc l{0, 0};
-    if (u < nu) {
-      const int t = u << p.log2_claim;
-      l.phys = min<int64_t>(max(bt_row[t >> p.log2_bs], 0), p.num_blocks - 1);
-      l.slot = t & (p.block_size - 1);
-    }
-    return l;
-  };
-  // chunk k (tokens k * CT) of a unit; in the matrix-core form the first chunk of a unit past
-  // the end is issued too, through resources of 0 records (the same loads on every path keep the
-  // compiler's wait counts exact; see run_range)
-  auto issue = [&](const Loc& l, int k, R& regs, bool live) {
-    if constexpr (!mq_form<D, G, HPI>()) {
-      if (!live) return;
-    }
-    const int64_t slot0 = l.slot + k * Gm::CT;
-    const int64_t rowb = (l.phys * p.c_sb + slot0 * p.c_ss) * esz;
-    const int64_t metab = (l.phys * p.m_sb + slot0 * p.m_ss) * 4;
-    load_chunk<D, HPI, KIND, G>(p, kc + rowb, vc + rowb, kmc + metab, vmc + metab, lo, c, regs, live);
-  };
-  int uc = take(__builtin_amdgcn_readfirstlane(claim_async()));
-  int un = take(__builtin_amdgcn_readfirstlane(claim_async()));
-  Loc pc = loc_of(uc);
-  R ra, rb;
-  issue(pc, 0, ra, uc < nu);
-  while (uc < nu) {
-    const int pending = (un < nu) ? claim_async() : 0;    // the claim after next
-    const Loc pn = loc_of(un);
-    const int tok = (uc << p.log2_claim) + tr;
-    for (int k = 0; k < my_n; k += 2) {
-      issue(pc, k + 1, rb, true);
-      __builtin_amdgcn_sched_barrier(0);
-      compute_chunk<D, G, BF16, KIND, HPI, false>(p, S, ra, tok + k * Gm::CT, 0, c);
-      if (k + 2 < my_n) issue(pc, k + 2, ra, true);
-      else issue(pn, 0, ra, un < nu);
-      __builtin_amdgcn_sched_barrier(0);
-      compute_chunk<D, G, BF16, KIND, HPI, false>(p, S, rb, tok + (k + 1) * Gm::CT, 0, c);
-    }
-    uc = un;
-    pc = pn;
-    un = (un < nu) ? take(__builtin_amdgcn_readfirstlane(pending)) : nu;
-  }
-}
-
 // Merge the rows of the wave that hold the same head at different token offsets (TPI > 1).
 template <int D, int G, CacheKind KIND, int HPI>
 __device__ __forceinline__ void merge_rows(State<G>& S) {
@@ -1176,9 +1093,7 @@ __device__ __forceinline__ int append_new_rows(const DecodeParams& p, int b, int
   return storing;
 }
 
-// CLAIM: compiled with the run-time hand-out of shared segments (p.claim_units set).
-// Kept out of the other instances so that its extra live state costs them no registers.
-template <int D, int G, bool BF16, CacheKind KIND, int HPI, bool CLAIM>
+template <int D, int G, bool BF16, CacheKind KIND, int HPI>
 __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) {
   using Gm = Geo<D, HPI, G>;
   extern __shared__ int s_pref[];              // batch + 1 entries
@@ -1323,26 +1238,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
       app_mine = (int)(threadIdx.x >> 6) < storing;
       new_tok = ctx - 1;
     }
-    auto range = [&](int ta, int tb) {
-      run_range<D, G, BF16, KIND, HPI>(p, S, b, hg, ta, tb, lane, tr, hh, c, cnt, new_tok, &s_app_done,
-                                       app_target, app_mine);
-      app_mine = false;
-    };
-    if constexpr (CLAIM) {
-      if (!(g0 == 0 && g1 == n)) {
-        // a shared segment: its full claim units by claim; the ragged tail (if any) by the
-        // workgroup that holds the segment's last granule
-        const int nu = ctx >> p.log2_claim;
-        run_claimed<D, G, BF16, KIND, HPI>(p, S, b, hg, nu,
-                                           p.ws_claim + ((int64_t)b * NHG + hg) * kClaimWaves + wv,
-                                           lane, tr, hh, c);
-        if (g1 == n && (nu << p.log2_claim) < ctx) range(nu << p.log2_claim, ctx);
-      } else {
-        range(t0, t1);
-      }
-    } else {
-      range(t0, t1);
-    }
+    run_range<D, G, BF16, KIND, HPI>(p, S, b, hg, t0, t1, lane, tr, hh, c, cnt, new_tok, &s_app_done,
+                                     app_target, app_mine);
     if constexpr (own_head_form<D, G>()) {      // every head's running sums into every lane
       quad_gather<G>(S.lo, S.l);
       if constexpr (KIND == CacheKind::U3) quad_gather<G>(S.zco, S.zc);
@@ -1412,48 +1309,47 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(DecodeParams p) 
 // so that the build can compile them in parallel.
 // ---------------------------------------------------------------------------------------
 template <int D, int G, bool BF16, CacheKind KIND, int HPI>
-const void* kernel_ptr(bool claim) {
-  return claim ? reinterpret_cast<const void*>(&decode_kernel<D, G, BF16, KIND, HPI, true>)
-               : reinterpret_cast<const void*>(&decode_kernel<D, G, BF16, KIND, HPI, false>);
+const void* kernel_ptr() {
+  return reinterpret_cast<const void*>(&decode_kernel<D, G, BF16, KIND, HPI>);
 }
 
 template <int D, int G, bool BF16, CacheKind KIND>
-const void* kernel_by_hpi(int hpi, bool claim) {
+const void* kernel_by_hpi(int hpi) {
   switch (hpi) {
-    case 1: return kernel_ptr<D, G, BF16, KIND, 1>(claim);
-    case 2: return kernel_ptr<D, G, BF16, KIND, 2>(claim);
-    case 4: return kernel_ptr<D, G, BF16, KIND, 4>(claim);
-    case 8: if constexpr (D == 64) return kernel_ptr<D, G, BF16, KIND, 8>(claim); else return nullptr;
+    case 1: return kernel_ptr<D, G, BF16, KIND, 1>();
+    case 2: return kernel_ptr<D, G, BF16, KIND, 2>();
+    case 4: return kernel_ptr<D, G, BF16, KIND, 4>();
+    case 8: if constexpr (D == 64) return kernel_ptr<D, G, BF16, KIND, 8>(); else return nullptr;
   }
   return nullptr;
 }
 
 template <int D, bool BF16, CacheKind KIND>
-const void* kernel_by_g(int group, int hpi, bool claim) {
+const void* kernel_by_g(int group, int hpi) {
   switch (group) {
-    case 1: return kernel_by_hpi<D, 1, BF16, KIND>(hpi, claim);
-    case 2: return kernel_by_hpi<D, 2, BF16, KIND>(hpi, claim);
-    case 4: return kernel_by_hpi<D, 4, BF16, KIND>(hpi, claim);
-    case 8: return kernel_by_hpi<D, 8, BF16, KIND>(hpi, claim);
+    case 1: return kernel_by_hpi<D, 1, BF16, KIND>(hpi);
+    case 2: return kernel_by_hpi<D, 2, BF16, KIND>(hpi);
+    case 4: return kernel_by_hpi<D, 4, BF16, KIND>(hpi);
+    case 8: return kernel_by_hpi<D, 8, BF16, KIND>(hpi);
   }
   return nullptr;
 }
 
 template <int D, CacheKind KIND>
-const void* kernel_by_dtype(int group, bool bf16, int hpi, bool claim) {
-  return bf16 ? kernel_by_g<D, true, KIND>(group, hpi, claim) : kernel_by_g<D, false, KIND>(group, hpi, claim);
+const void* kernel_by_dtype(int group, bool bf16, int hpi) {
+  return bf16 ? kernel_by_g<D, true, KIND>(group, hpi) : kernel_by_g<D, false, KIND>(group, hpi);
 }
 
-// host pointer of decode_kernel<D, group, bf16, KIND, hpi, claim>, or nullptr if not built
-const void* decode_kernel_ptr_same_d128(int group, bool bf16, int hpi, bool claim);
-const void* decode_kernel_ptr_same_d64(int group, bool bf16, int hpi, bool claim);
-const void* decode_kernel_ptr_fp8_d128(int group, bool bf16, int hpi, bool claim);
-const void* decode_kernel_ptr_fp8_d64(int group, bool bf16, int hpi, bool claim);
-const void* decode_kernel_ptr_u3_d128(int group, bool bf16, int hpi, bool claim);
-const void* decode_kernel_ptr_u3_d64(int group, bool bf16, int hpi, bool claim);
-const void* decode_kernel_ptr_e5m2_d128(int group, bool bf16, int hpi, bool claim);
-const void* decode_kernel_ptr_e5m2_d64(int group, bool bf16, int hpi, bool claim);
-const void* decode_kernel_ptr_i8_d128(int group, bool bf16, int hpi, bool claim);
-const void* decode_kernel_ptr_i8_d64(int group, bool bf16, int hpi, bool claim);
+// host pointer of decode_kernel<D, group, bf16, KIND, hpi>, or nullptr if not built
+const void* decode_kernel_ptr_same_d128(int group, bool bf16, int hpi);
+const void* decode_kernel_ptr_same_d64(int group, bool bf16, int hpi);
+const void* decode_kernel_ptr_fp8_d128(int group, bool bf16, int hpi);
+const void* decode_kernel_ptr_fp8_d64(int group, bool bf16, int hpi);
+const void* decode_kernel_ptr_u3_d128(int group, bool bf16, int hpi);
+const void* decode_kernel_ptr_u3_d64(int group, bool bf16, int hpi);
+const void* decode_kernel_ptr_e5m2_d128(int group, bool bf16, int hpi);
+const void* decode_kernel_ptr_e5m2_d64(int group, bool bf16, int hpi);
+const void* decode_kernel_ptr_i8_d128(int group, bool bf16, int hpi);
+const void* decode_kernel_ptr_i8_d64(int group, bool bf16, int hpi);
 
 }  // namespace pkv

@@ -65,9 +65,6 @@ struct DecodeParams {
   float* ws_acc;                      // [num_wgs, 2, heads_per_group, G, D] partial accumulators
   float* ws_ml;                       // [num_wgs, 2, heads_per_group, G, 2] partial (m, l)
   int* ws_seg;                        // [batch, head groups, 2] first partial slot, last owner
-  int* ws_claim;                      // [batch, head groups, 4] unit counters (cleared by each call)
-  int claim_units;                    // shared segments hand out their tokens dynamically ...
-  int log2_claim;                     // ... in units of 2^log2_claim tokens inside one block
   // fused append of a decode step (paged_decode_append): request b's new K and V rows,
   // [batch, num_kv_heads, head_dim] of the query dtype, are written at position
   // context_lens[b] - 1 before the decode reads it; nullptr: no append

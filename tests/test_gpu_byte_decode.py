@@ -115,12 +115,12 @@ def test_byte_decode_llama8b_full_size_sampled(kind):
 
 
 @pytest.mark.parametrize("kind", KINDS)
-def test_byte_decode_block_claiming_ragged(kind):
-    """64-token blocks (a wave's share of a block is 66 KB of codes and scales, so shared
-    segments hand out their blocks at run time); the same workspace three times."""
+def test_byte_decode_large_blocks_ragged(kind):
+    """64-token blocks (a wave's share of a block is 66 KB of codes and scales), ragged contexts
+    shared by several workgroups; the same workspace three times."""
     P = need_gpu()
     lens = [1, 63, 64, 65, 5000, 20011, 129, 12345]
-    wl = W.decode_workload(f"{kind}-claims", batch=len(lens), num_q_heads=32, num_kv_heads=8,
+    wl = W.decode_workload(f"{kind}-large-blocks", batch=len(lens), num_q_heads=32, num_kv_heads=8,
                            head_dim=128, block_size=64, ctx_lo=0, ctx_hi=0, dtype=torch.bfloat16,
                            device="cuda", seed=W.BASE_SEED + 33, append_one=False, ctx_override=lens)
     gpu = _pools_gpu(P, wl, kind)
@@ -134,7 +134,7 @@ def test_byte_decode_block_claiming_ragged(kind):
         out = P.paged_decode(wl.q, gpu[0], gpu[1], wl.block_tables.cuda(), wl.ctx_after.cuda(),
                              max(lens), wl.sm_scale, k_meta=gpu[2], v_meta=gpu[3], workspace=ws,
                              cache_dtype=kind)
-        assert report(f"{kind} claims rep{rep}", f32_of(out), want, wl.dtype) <= ATTN_TOL
+        assert report(f"{kind} large blocks rep{rep}", f32_of(out), want, wl.dtype) <= ATTN_TOL
 
 
 # ---- caller-given scales (kv_append_scaled / paged_decode_scaled): "Write Triton Kv Cache

@@ -227,8 +227,7 @@ def test_rejects_bad_arguments():
 
 def test_workspace_reused_across_calls():
     """One workspace serves consecutive calls of different batch sizes and partition sizes: each
-    call clears the block counters it claims from and overwrites every partial state and segment
-    record it reads."""
+    call overwrites every partial state and segment record it reads."""
     P = need_gpu()
     big = W.llama8b_decode("cuda", batch=48, seed=W.BASE_SEED + 21)
     small = W.llama8b_decode("cuda", batch=5, seed=W.BASE_SEED + 22)
@@ -246,31 +245,30 @@ def test_workspace_reused_across_calls():
                       wl.dtype) <= ATTN_TOL
 
 
-def test_block_claiming_ragged():
-    """Contexts shared by several workgroups whose 64-token blocks (128 KB of a wave's K/V) are
-    handed out at run time: ragged lengths, one-block and one-token contexts, all heads."""
+def test_large_blocks_ragged():
+    """64-token blocks (128 KB of a wave's K/V per block), contexts shared by several
+    workgroups: ragged lengths, one-block and one-token contexts, all heads; the same workspace
+    three times."""
     P = need_gpu()
     lens = [1, 63, 64, 65, 5000, 20011, 129, 12345]
-    wl = W.decode_workload("claims", batch=len(lens), num_q_heads=32, num_kv_heads=8, head_dim=128,
+    wl = W.decode_workload("large-blocks", batch=len(lens), num_q_heads=32, num_kv_heads=8, head_dim=128,
                            block_size=64, ctx_lo=0, ctx_hi=0, dtype=torch.bfloat16, device="cuda",
                            seed=W.BASE_SEED + 31, append_one=False, ctx_override=lens)
     ws = P.decode_workspace(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, max(lens), 0)
     want = _oracle_same(wl, wl.k_pool, wl.v_pool, wl.ctx_after)
-    for rep in range(3):                  # the same workspace: the counters restart at zero
+    for rep in range(3):
         out = _decode(P, wl, wl.k_pool, wl.v_pool, wl.ctx_after, workspace=ws)
-        assert report(f"claims rep {rep}", f32_of(out), want, wl.dtype) <= ATTN_TOL
+        assert report(f"large blocks rep {rep}", f32_of(out), want, wl.dtype) <= ATTN_TOL
 
 
 @pytest.mark.parametrize("fill", ["small-counts", "ones", "random"])
 def test_workspace_any_contents(fill):
-    """The workspace may hold anything when a call starts.  The block hand-out counters are the
-    part a call would otherwise read before writing: filled with small counts inside the claim
-    range (the case that would skip blocks silently), all-ones bytes or random bytes, the
-    claimed long-context path matches the oracle at partition sizes 16 and 512, on every one of
-    three calls."""
+    """The workspace may hold anything when a call starts: filled before each of three calls with
+    small counts, all-ones bytes or random bytes, the decode over 64-token blocks and long
+    contexts matches the oracle at partition sizes 16 and 512."""
     P = need_gpu()
     lens = [1, 63, 64, 65, 5000, 20011, 129, 12345]
-    wl = W.decode_workload("claims-dirty", batch=len(lens), num_q_heads=32, num_kv_heads=8,
+    wl = W.decode_workload("dirty-workspace", batch=len(lens), num_q_heads=32, num_kv_heads=8,
                            head_dim=128, block_size=64, ctx_lo=0, ctx_hi=0, dtype=torch.bfloat16,
                            device="cuda", seed=W.BASE_SEED + 32, append_one=False, ctx_override=lens)
     want = _oracle_same(wl, wl.k_pool, wl.v_pool, wl.ctx_after)
@@ -385,12 +383,12 @@ def test_fp8_decode_llama8b_full_size_sampled():
     assert report("fp8 llama8b", f32_of(out)[sel], want[sel], wl.dtype) <= ATTN_TOL
 
 
-def test_fp8_decode_block_claiming_ragged():
-    """fp8 pools with 64-token blocks (a wave's share of a block is 66 KB of codes and scales,
-    so shared segments hand out their blocks at run time); the same workspace three times."""
+def test_fp8_decode_large_blocks_ragged():
+    """fp8 pools with 64-token blocks (a wave's share of a block is 66 KB of codes and scales),
+    ragged contexts shared by several workgroups; the same workspace three times."""
     P = need_gpu()
     lens = [1, 63, 64, 65, 5000, 20011, 129, 12345]
-    wl = W.decode_workload("fp8-claims", batch=len(lens), num_q_heads=32, num_kv_heads=8,
+    wl = W.decode_workload("fp8-large-blocks", batch=len(lens), num_q_heads=32, num_kv_heads=8,
                            head_dim=128, block_size=64, ctx_lo=0, ctx_hi=0, dtype=torch.bfloat16,
                            device="cuda", seed=W.BASE_SEED + 32, append_one=False, ctx_override=lens)
     gpu = _fp8_pools_gpu(P, wl)
@@ -403,13 +401,12 @@ def test_fp8_decode_block_claiming_ragged():
     for rep in range(3):
         out = P.paged_decode(wl.q, gpu[0], gpu[1], wl.block_tables.cuda(), wl.ctx_after.cuda(),
                              max(lens), wl.sm_scale, k_meta=gpu[2], v_meta=gpu[3], workspace=ws)
-        assert report(f"fp8 claims rep {rep}", f32_of(out), want, wl.dtype) <= ATTN_TOL
+        assert report(f"fp8 large blocks rep {rep}", f32_of(out), want, wl.dtype) <= ATTN_TOL
 
 
 def test_one_workspace_serves_every_cache_kind():
     """A workspace sized by paged_decode_workspace_size (which plans for every cache kind) serves
-    bf16, fp8 and 3-bit decodes in turn, and the 64-token-block fp8 call with run-time block
-    hand-out in between leaves it usable for the next."""
+    bf16, fp8 and 3-bit decodes over 64-token blocks in turn, each on what the one before left."""
     P = need_gpu()
     lens = [700, 1, 4100, 64, 0, 2048]
     same = W.decode_workload("mix-same", batch=len(lens), num_q_heads=32, num_kv_heads=8, head_dim=128,

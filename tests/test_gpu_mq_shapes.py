@@ -3,10 +3,9 @@
 The form applies where a wave instruction holds one token of as many kv heads as its lanes
 cover (4 heads of head_dim 128, 8 of head_dim 64) and a kv head serves 2, 4 or 8 query heads:
 the shapes with 8 kv heads here.  Every cache kind (16-bit, fp8 e4m3fn, fp8 e5m2, int8, 3-bit)
-at each such group size, both head dims, blocks of 16 and 64 tokens (64: the run-time block
-hand-out for contexts that several workgroups share), fp16 and bf16 queries, two partition
-sizes; contexts ragged against the 4-token chunks and 16-token blocks, one empty, and the
-pools' unused slots NaN-poisoned where the cache holds 16-bit values.
+at each such group size, both head dims, blocks of 16 and 64 tokens, fp16 and bf16 queries,
+two partition sizes; contexts ragged against the 4-token chunks and 16-token blocks, one empty,
+and the pools' unused slots NaN-poisoned where the cache holds 16-bit values.
 
 Pages: "Triton KV Cache and PagedAttention", Step 1 and the reference answer TODO 1-5 (the
 attention); "Write Triton Kv Cache Append Kernel", Inputs item 4 (byte-code caches read back

@@ -2,9 +2,8 @@
 the library's static device scratch) against paged_decode, through the C ABI.
 
 Two calls in a row on the same GPU, the second with a smaller input, so the second call runs on
-scratch the first one left behind: the long-context shape on the run-time block hand-out path
-(64-token blocks; its counters must be cleared by the call itself), then a small Llama-8B-shaped
-batch on the static split.  Each output is checked against the oracle (the attention tolerance:
+scratch the first one left behind: a long-context shape (64-token blocks), then a small
+Llama-8B-shaped batch.  Each output is checked against the oracle (the attention tolerance:
 2e-3 plus half a unit in the last place of the output dtype) and against paged_decode's output
 on the same inputs (the decode's summation order depends on timing, so two correct results
 differ by at most twice that tolerance).  A call beyond the scratch's limit is rejected."""
@@ -48,7 +47,7 @@ def _check(tag, wl, got, ref, want, sel=None):
 
 def test_noalloc_matches_paged_decode_two_calls():
     P = need_gpu()
-    # call 1: long context on the claimed path (batch 3, 64 / 8 heads, 64-token blocks)
+    # call 1: long context (batch 3, 64 / 8 heads, 64-token blocks)
     lens = [40000, 70001, 33333]
     big = W.decode_workload("noalloc-long", batch=len(lens), num_q_heads=64, num_kv_heads=8,
                             head_dim=128, block_size=64, ctx_lo=0, ctx_hi=0, dtype=torch.bfloat16,
