@@ -74,6 +74,28 @@ def test_llama8b_full_size_all_heads():
     assert report("llama8b", f32_of(out), want, wl.dtype) <= ATTN_TOL
 
 
+@pytest.mark.parametrize("Hq,Hkv,D,bs", [(32, 8, 128, 16), (64, 8, 128, 16), (16, 8, 64, 16),
+                                         (8, 8, 128, 32)])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_many_requests_few_partials(Hq, Hkv, D, bs, dtype):
+    """72 requests: enough that a split segment holds only a few partial states, which the merge
+    takes in one pass, several elements per thread.  Empty, one-token and ragged contexts, all
+    heads, NaN-poisoned unused slots."""
+    P = need_gpu()
+    rng = np.random.default_rng(900 + Hq + D + bs)
+    lens = rng.integers(2, 700, size=72)
+    lens[[0, 5, 17, 40, 71]] = 0
+    lens[[1, 33]] = 1
+    wl = W.decode_workload("few-partials", batch=len(lens), num_q_heads=Hq, num_kv_heads=Hkv,
+                           head_dim=D, block_size=bs, ctx_lo=0, ctx_hi=0, dtype=dtype, device="cuda",
+                           seed=W.BASE_SEED + 51, append_one=False, ctx_override=[int(x) for x in lens])
+    out = _decode(P, wl, wl.k_pool, wl.v_pool, wl.ctx_after)
+    want = _oracle_same(wl, wl.k_pool, wl.v_pool, wl.ctx_after)
+    assert np.all(f32_of(out)[lens == 0] == 0)
+    assert report(f"few partials Hq{Hq} D{D} bs{bs} {dtype_name(dtype)}", f32_of(out), want,
+                  dtype) <= ATTN_TOL
+
+
 @pytest.mark.parametrize("ps", [0, 16, 256, 512, 4096])
 def test_partition_sizes_agree(ps):
     P = need_gpu()
