@@ -1,4 +1,4 @@
-// Paged decode attention: the split-K merge kernel and the host side (grid plan, dispatch).
+// Paged decode attention: the split-K merge kernels and the host side (grid plan, dispatch).
 // The decode kernel itself is in decode_kernel.cuh.
 #include <algorithm>
 
@@ -272,7 +272,8 @@ hipError_t launch_decode(const DecodeParams& p, const DecodePlan& plan, CacheKin
   hipError_t e = hipLaunchKernel(fn, dim3((unsigned)plan.num_wgs), dim3(plan.waves_per_wg * 64), args,
                       plan.lds_bytes, s);
   if (e != hipSuccess) return e;
-  // split the partials of a segment so that each thread merges about 2 x kMergeBatch of them
+  // split the partials of a segment so that each thread merges about 2 x kMergeBatch of them;
+  // where one split suffices, the one-pass form with several elements per thread
   const int64_t per_seg = plan.num_wgs / std::max<int64_t>(1, (int64_t)p.batch * plan.num_head_groups) + 2;
   int splits = 1;
   while (splits < kMergeMaxSplit && per_seg > (int64_t)splits * 2 * kMergeBatch) splits *= 2;
