@@ -417,11 +417,11 @@ def run_llama8b(args, P, W):
         "append_timing": "kv_append alone, graph replay of the 4 per-layer appends (launch-bound)",
     })
     if args.separate_append:
-        rec["roofline"] = hbm_roofline("paged_decode (decode_kernel + merge_kernel)", dec_bytes_all,
+        rec["roofline"] = hbm_roofline("paged_decode (decode_kernel + merge)", dec_bytes_all,
                                        dec_ms, recorded_traffic("paged_decode"))
     else:
         rec["step_us"] = stats_us(step_ms)
-        rec["roofline"] = hbm_roofline("paged_decode_append (decode_kernel with the step's append + merge_kernel)",
+        rec["roofline"] = hbm_roofline("paged_decode_append (decode_kernel with the step's append + merge)",
                                        dec_bytes_all + app_b, step_ms, recorded_traffic("paged_decode_append"))
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl0, host_k, host_v)
@@ -537,7 +537,7 @@ def run_long_context(args, P, W):
               "partition_size": ps, "kv_bytes": kv}
     rec = base_record(args, "paged decode KV GB/s (long context, split-K)",
                       alg / (st["median"] * 1e-6) / 1e9, "GB/s", ms_per_step, "bf16", config)
-    rec.update({"decode_us": st, "roofline": hbm_roofline("paged_decode (decode_kernel + merge_kernel)",
+    rec.update({"decode_us": st, "roofline": hbm_roofline("paged_decode (decode_kernel + merge)",
                                                           alg, ms)})
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = decode_cpu_baseline(
@@ -596,7 +596,7 @@ def run_packed3(args, P, W):
               "partition_size": ps or "auto"}
     rec = base_record(args, "paged decode KV GB/s (3-bit packed cache)",
                       alg / (st["median"] * 1e-6) / 1e9, "GB/s", ms_per_step, "f16", config)
-    rec.update({"decode_us": st, "roofline": hbm_roofline("paged_decode (decode_kernel u3 + merge_kernel)",
+    rec.update({"decode_us": st, "roofline": hbm_roofline("paged_decode (decode_kernel u3 + merge)",
                                                           alg, ms)})
     if not args.no_cpu_baseline:
         kc, vc, km, vm = pools[0]
@@ -679,7 +679,7 @@ def run_fp8_decode(args, P, W, kind="fp8", per_tensor=False):
     rec = base_record(args, f"paged decode KV GB/s ({label} cache{', per-tensor scale' if per_tensor else ''})",
                       alg / (st["median"] * 1e-6) / 1e9, "GB/s", ms_per_step, "bf16", config)
     rec.update({"decode_us": st, "context_tokens_per_s": round(tokens / (st["median"] * 1e-6), 1),
-                "roofline": hbm_roofline(f"paged_decode (decode_kernel {kind} + merge_kernel)", alg, ms)})
+                "roofline": hbm_roofline(f"paged_decode (decode_kernel {kind} + merge)", alg, ms)})
     if not args.no_cpu_baseline:
         w, kc, vc, km, vm = pools[0]
         rec["cpu_baseline"] = decode_cpu_baseline(
@@ -752,7 +752,7 @@ def run_contiguous(args, P, W):
               "layers_rotated": N_LAYERS, "partition_size": args.partition_size or "auto"}
     rec = base_record(args, "paged decode KV GB/s (contiguous cache)",
                       alg / (st["median"] * 1e-6) / 1e9, "GB/s", ms_per_step, "bf16", config)
-    rec.update({"decode_us": st, "roofline": hbm_roofline("paged_decode (decode_kernel + merge_kernel)", alg,
+    rec.update({"decode_us": st, "roofline": hbm_roofline("paged_decode (decode_kernel + merge)", alg,
                                                           ms)})
     if not args.no_cpu_baseline:
         w, _, views, table, ctx, _ = layers[0]
@@ -813,7 +813,7 @@ def run_dual_stacked(args, P, W):
               "partition_size": args.partition_size or "auto"}
     rec = base_record(args, "paged decode KV GB/s (dual-stacked block layout)",
                       alg / (st["median"] * 1e-6) / 1e9, "GB/s", ms_per_step, "bf16", config)
-    rec.update({"decode_us": st, "roofline": hbm_roofline("paged_decode (decode_kernel + merge_kernel)", alg,
+    rec.update({"decode_us": st, "roofline": hbm_roofline("paged_decode (decode_kernel + merge)", alg,
                                                           ms)})
     if not args.no_cpu_baseline:
         w, _, kc, vc, bt, ctx, _ = layers[0]
