@@ -534,12 +534,15 @@ __device__ __forceinline__ void compute_chunk(const DecodeParams& p, State<G>& S
       if constexpr (KIND == CacheKind::U3) {
         // q.(code - z)*s = s * (q.code - z * sum(q)); bf16 codes carry +128 (folded into z);
         // fp16: sacc is q.code * 2^-24 and S.qso the query sum * 2^-24
-        const float ks = f16_lo(kmt[i]), kz = f16_hi(kmt[i]);
+        const float kz = f16_hi(kmt[i]);
         const float off = BF16 ? 128.f + kz : kz;
         const float kscl = BF16 ? p.scale_log2 : p.scale_log2 * 0x1p24f;
+        // the scale times the score factor in one mixed-precision fma on the stored fp16 scale,
+        // then one product per head
+        const float ks2 = fmaf(f16_lo(kmt[i]), kscl, 0.f);
 #pragma unroll
         for (int h = 0; h < HO; ++h)
-          sco[i][h] = valid[i] ? ks * (sacc[h][i] - off * S.qso[h]) * kscl : neg_inf();
+          sco[i][h] = valid[i] ? ks2 * (sacc[h][i] - off * S.qso[h]) : neg_inf();
       } else {
         float scl = p.scale_log2;
         if constexpr (byte_kind(KIND)) scl *= __uint_as_float(kmt[i]);
